@@ -1,0 +1,80 @@
+"""Seeded synthetic inputs for the block-FP8 decode GEMM.
+
+This module only draws random numbers and rounds them to the input dtypes;
+it contains none of the quantisation or GEMM arithmetic. Both the CPU oracle
+tests and the HIP-path tests and benchmark take their inputs from here.
+
+The pages measure real Qwen3.8-27B-FP8 weights on ShareGPT prompts (page 1,
+section "test background"), a 3,465-token prompt (page 2, section 5) and
+256-token prompts (page 3, section 2.3). None of that data is available, and
+the GEMM's cost does not depend on the values, so Gaussian stand-ins with the
+pages' shapes replace them:
+
+* weights: W = 0.02 * N(0, 1) in fp32, shape [N, K];
+* activations: A = N(0, 1), with 0.1 % of the entries (at least one, at
+  uniformly drawn distinct positions) multiplied by 20 as outliers, rounded
+  to bf16 (round-to-nearest-even via torch);
+* the tiny case (M=1, N=512, K=1024) uses one generator seeded 0, drawing W
+  first and then A, with no outliers.
+
+Seeds: W for shape (N, K) comes from ``numpy.random.default_rng([0, N, K])``;
+A for (M, N, K) from ``default_rng([0, N, K, M])``, normals first, outlier
+positions second.
+"""
+
+import numpy as np
+import torch
+
+# The five (N, K) shapes logged in page 2 (ownding.com L20 report), section 8.
+SHAPES = [(17408, 5120), (5120, 3072), (5120, 8704), (7168, 5120), (8192, 5120)]
+TINY = (1, 512, 1024)  # (M, N, K)
+PREFILL_M = 3465  # prompt length of page 2's test protocol (section 5)
+PREFILL_SHAPES = [(17408, 5120), (5120, 8704)]
+OUTLIER_FRACTION = 0.001
+OUTLIER_FACTOR = 20.0
+
+
+def to_bf16(x: np.ndarray) -> torch.Tensor:
+    """fp32 numpy -> bf16 CPU tensor, round to nearest even."""
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def tiny_inputs():
+    """(A bf16 [1, 1024], W fp32 [512, 1024]) of the tiny case, seed 0."""
+    m, n, k = TINY
+    rng = np.random.default_rng(0)
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    a = rng.standard_normal((m, k)).astype(np.float32)
+    return to_bf16(a), w
+
+
+def weight(n: int, k: int) -> np.ndarray:
+    """W fp32 [N, K] = 0.02 * N(0, 1), seeded by the shape."""
+    rng = np.random.default_rng([0, n, k])
+    return (0.02 * rng.standard_normal((n, k), dtype=np.float32)).astype(np.float32)
+
+
+def activation(m: int, n: int, k: int, outliers: bool = True) -> torch.Tensor:
+    """A bf16 [M, K] = N(0, 1) with 0.1 % outliers x20, seeded by (N, K, M)."""
+    rng = np.random.default_rng([0, n, k, m])
+    a = rng.standard_normal((m, k), dtype=np.float32)
+    if outliers and m * k > 0:
+        count = max(1, int(round(OUTLIER_FRACTION * m * k)))
+        idx = rng.choice(m * k, size=count, replace=False)
+        flat = a.reshape(-1)
+        flat[idx] = flat[idx] * np.float32(OUTLIER_FACTOR)
+    return to_bf16(a)
+
+
+def random_codes(shape, seed: int) -> np.ndarray:
+    """Uniform e4m3fn codes over all 254 finite codes (NaN codes excluded)."""
+    rng = np.random.default_rng(seed)
+    c = rng.integers(0, 254, size=shape, dtype=np.int64)
+    c = c + (c >= 0x7F)  # skip 0x7F; 0xFF is never drawn
+    return c.astype(np.uint8)
+
+
+def random_scales(shape, seed: int, lo: float = 2.0 ** -12, hi: float = 2.0 ** -4) -> np.ndarray:
+    """Positive fp32 scales, log-uniform in [lo, hi)."""
+    rng = np.random.default_rng(seed)
+    return np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape)).astype(np.float32)
