@@ -1,0 +1,134 @@
+/*
+ * fp8bq -- W8A8 block-FP8 linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the weight GEMM of a dense decoder's linear layer,
+ * y = x W^T, with W stored as "W8A8 Block FP8" of shape (N, K) -- page 2
+ * (ownding.com, "Qwen3.8-27B-FP8 + MTP tuning report on two NVIDIA L20"),
+ * section 8 "L20 FP8 Kernel tuning experiment", which lists the five logged
+ * (N, K) shapes; page 1 (SmartX blog, "Qwen3.8-27B performance
+ * optimisation"), section "single-stream optimisation", which says the W8A8
+ * backend quantises the activation on every call; and the same page's
+ * section "operator optimisation", which puts about 89% of each decode step
+ * in these weight-reading matmuls.
+ *
+ * Number format (the pages say only "FP8"; the block scheme is the
+ * DeepSeek-style one page 2's tuning script targets):
+ *   - codes are OCP e4m3fn bytes (bias 7, max 448, no infinities, 0x7F/0xFF
+ *     NaN); a value is decode(code) * scale;
+ *   - activations: one fp32 scale per token per 128 consecutive K entries;
+ *   - weights: one fp32 scale per 128 x 128 block (rows 128b.., cols 128g..);
+ *   - scale = amax / 448 (IEEE fp32 division), 1.0 for an all-zero group;
+ *     codes = RNE(clamp(x / scale, -448, 448)).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device; all
+ *     tensors are dense row-major. The caller owns every buffer; the library
+ *     allocates nothing, keeps no pointer after return and has no state
+ *     beyond a per-device capability check.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work
+ *     on it and return without synchronising; faults during execution
+ *     surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued. On
+ *     error nothing is launched and a negative fp8bq_status is returned.
+ *   - M == 0 or N == 0 is a quick return (FP8BQ_OK, nothing launched).
+ *   - Outputs must not alias inputs. NaN/Inf activations or weights and
+ *     NaN weight codes (0x7F, 0xFF) give unspecified results.
+ *   - Calls on different streams are independent and may run concurrently.
+ */
+#ifndef FP8BQ_H
+#define FP8BQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8bq_status {
+    FP8BQ_OK = 0,
+    FP8BQ_ERR_NULL = -1,   /* a required pointer is NULL                     */
+    FP8BQ_ERR_SHAPE = -2,  /* a size is negative, K % 128 != 0, or too large  */
+    FP8BQ_ERR_ALIGN = -3,  /* code/bf16 pointer not 16-B aligned, fp32 not 4-B */
+    FP8BQ_ERR_DEVICE = -4, /* no HIP device, or the current device is not gfx950 */
+    FP8BQ_ERR_LAUNCH = -5  /* the HIP runtime rejected a kernel launch        */
+} fp8bq_status;
+
+/*
+ * Per-token activation quantisation (page 1, "single-stream optimisation":
+ * the per-call activation-quantisation launch of the W8A8 backend).
+ *
+ *   A_bf16   [M, K] bf16, read.
+ *   A_fp8    [M, K] uint8 e4m3fn codes, written.
+ *   A_scales [M, K/128] fp32, written; A_scales[m, g] is the scale of
+ *            A_bf16[m, 128g .. 128g+127].
+ * Bit-exact: codes and scales equal the definition above for every finite
+ * input (fp32 amax, IEEE division, RNE to e4m3fn, signed zero kept).
+ * Errors: NULL pointer; M < 0, K < 0 or K % 128 != 0; M*K > 2^40; A_bf16 or
+ * A_fp8 not 16-B aligned, A_scales not 4-B aligned; device not gfx950.
+ */
+int fp8bq_quant_act(int64_t M, int64_t K, const void *A_bf16, void *A_fp8, float *A_scales,
+                    void *stream);
+
+/*
+ * Per-128x128-block weight quantisation (page 2, section 8: the weights of
+ * each logged shape are stored as W8A8 block FP8). The pages' checkpoints
+ * arrive pre-quantised; this call builds such weights from fp32 on the GPU.
+ *
+ *   W_f32    [N, K] fp32, read. N arbitrary: the last row block may be short.
+ *   W_fp8    [N, K] uint8 e4m3fn codes, written.
+ *   W_scales [ceil(N/128), K/128] fp32, written.
+ * Bit-exact with the same rule as fp8bq_quant_act, amax taken per block.
+ * Errors: as fp8bq_quant_act (W_f32 must be 16-B aligned).
+ */
+int fp8bq_quant_weight(int64_t N, int64_t K, const float *W_f32, void *W_fp8, float *W_scales,
+                       void *stream);
+
+/*
+ * Block-scaled FP8 GEMM (page 2, section 8: the W8A8 block-FP8 matmul of
+ * shape (N, K) at batch size M; page 1, "operator optimisation": the
+ * weight-reading matmuls that bound the decode step).
+ *
+ *   C[m, n] = sum_g A_scales[m, g] * W_scales[n / 128, g]
+ *                   * sum_{k = 128g}^{128g+127} dec(A_fp8[m, k]) * dec(W_fp8[n, k])
+ *
+ *   A_fp8    [M, K] uint8 codes,  A_scales [M, K/128] fp32          (read)
+ *   W_fp8    [N, K] uint8 codes,  W_scales [ceil(N/128), K/128] fp32 (read)
+ *   C_bf16   [M, N] bf16, written, fp32 accumulation rounded to bf16 RNE.
+ * Every M >= 1 is served by a kernel chosen from explicit M ranges (no
+ * nearest-size table). The summation order differs from the fp64
+ * definition; results agree within fp32 accumulation plus bf16 rounding.
+ * Two identical calls give bitwise-identical C (no atomics).
+ * K == 0 writes zeros. Errors: NULL pointer; negative size; K % 128 != 0;
+ * M*K, N*K or M*N > 2^40; code/bf16 pointers not 16-B aligned, scale
+ * pointers not 4-B aligned; device not gfx950.
+ */
+int fp8bq_gemm(int64_t M, int64_t N, int64_t K, const void *A_fp8, const float *A_scales,
+               const void *W_fp8, const float *W_scales, void *C_bf16, void *stream);
+
+/*
+ * Kernel-path introspection for tests and profiling. Returns the path
+ * fp8bq_gemm would take for (M, N, K) -- FP8BQ_PATH_STREAM for the
+ * weight-streaming split-K kernel, FP8BQ_PATH_TILED for the LDS-tiled MFMA
+ * kernel -- or a negative status for invalid sizes.
+ */
+enum { FP8BQ_PATH_NONE = 0, FP8BQ_PATH_STREAM = 1, FP8BQ_PATH_TILED = 2 };
+int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K);
+
+/*
+ * fp8bq_gemm with the kernel path forced (FP8BQ_PATH_STREAM requires
+ * M <= 64; FP8BQ_PATH_TILED accepts any M). For cross-checking the two paths
+ * at the same M. Same arguments, semantics and errors as fp8bq_gemm, plus
+ * FP8BQ_ERR_SHAPE for a path that cannot serve M.
+ */
+int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_fp8,
+                      const float *A_scales, const void *W_fp8, const float *W_scales,
+                      void *C_bf16, void *stream);
+
+/* Human-readable name of a status code; never NULL. */
+const char *fp8bq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BQ_H */

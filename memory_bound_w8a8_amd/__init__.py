@@ -1,0 +1,168 @@
+"""Python binding of libfp8bq (W8A8 block-FP8 linear layer on MI355X).
+
+Argument marshalling only: every step runs in the HIP kernels of
+libfp8bq.so, called through its C ABI (include/fp8bq.h). torch supplies
+device memory and the current stream. There is no fallback: if the library
+is missing or cannot run, the calls raise.
+
+    a_q, a_s = quant_act(a)              # a: bf16 [M, K] on the GPU
+    w_q, w_s = quant_weight(w)           # w: fp32 [N, K] on the GPU
+    c = gemm(a_q, a_s, w_q, w_s)         # c: bf16 [M, N]
+"""
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp8bq.so")
+
+FP8BQ_OK = 0
+PATH_NONE, PATH_STREAM, PATH_TILED = 0, 1, 2
+PATH_NAMES = {PATH_NONE: "none", PATH_STREAM: "stream", PATH_TILED: "tiled"}
+
+# Every symbol the C ABI exports (kept in step with include/fp8bq.h).
+EXPORTS = (
+    "fp8bq_quant_act",
+    "fp8bq_quant_weight",
+    "fp8bq_gemm",
+    "fp8bq_gemm_path",
+    "fp8bq_gemm_forced",
+    "fp8bq_status_string",
+)
+
+
+class Fp8bqError(RuntimeError):
+    """A nonzero status returned by libfp8bq."""
+
+    def __init__(self, call: str, status: int):
+        super().__init__(f"{call}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfp8bq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m memory_bound_w8a8_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, fp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p
+        L.fp8bq_quant_act.argtypes = [i64, i64, vp, vp, fp, vp]
+        L.fp8bq_quant_weight.argtypes = [i64, i64, fp, vp, fp, vp]
+        L.fp8bq_gemm.argtypes = [i64, i64, i64, vp, fp, vp, fp, vp, vp]
+        L.fp8bq_gemm_forced.argtypes = [ctypes.c_int, i64, i64, i64, vp, fp, vp, fp, vp, vp]
+        L.fp8bq_gemm_path.argtypes = [i64, i64, i64]
+        L.fp8bq_status_string.argtypes = [ctypes.c_int]
+        L.fp8bq_status_string.restype = ctypes.c_char_p
+        for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fp8bq_status_string(int(status)).decode()
+
+
+def _check(call: str, status: int) -> None:
+    if status != FP8BQ_OK:
+        raise Fp8bqError(call, status)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _codes(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be on a GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {ndim}-d tensor")
+
+
+def quant_act(a: torch.Tensor):
+    """bf16 [M, K] -> (uint8 e4m3fn codes [M, K], fp32 scales [M, K/128])."""
+    _need(a, "a", torch.bfloat16, 2)
+    m, k = a.shape
+    a_q = torch.empty((m, k), dtype=torch.uint8, device=a.device)
+    a_s = torch.empty((m, k // 128 if k % 128 == 0 else 0), dtype=torch.float32, device=a.device)
+    with torch.cuda.device(a.device):
+        _check("fp8bq_quant_act", lib().fp8bq_quant_act(m, k, _ptr(a), _ptr(a_q), _ptr(a_s), _stream(a)))
+    return a_q, a_s
+
+
+def quant_weight(w: torch.Tensor):
+    """fp32 [N, K] -> (uint8 codes [N, K], fp32 scales [ceil(N/128), K/128])."""
+    _need(w, "w", torch.float32, 2)
+    n, k = w.shape
+    w_q = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    w_s = torch.empty(((n + 127) // 128, k // 128 if k % 128 == 0 else 0), dtype=torch.float32, device=w.device)
+    with torch.cuda.device(w.device):
+        _check("fp8bq_quant_weight", lib().fp8bq_quant_weight(n, k, _ptr(w), _ptr(w_q), _ptr(w_s), _stream(w)))
+    return w_q, w_s
+
+
+def _gemm_args(a_q, a_s, w_q, w_s, out):
+    a_q, w_q = _codes(a_q), _codes(w_q)
+    _need(a_q, "a_q", torch.uint8, 2)
+    _need(w_q, "w_q", torch.uint8, 2)
+    _need(a_s, "a_s", torch.float32, 2)
+    _need(w_s, "w_s", torch.float32, 2)
+    m, k = a_q.shape
+    n, k2 = w_q.shape
+    if k != k2:
+        raise ValueError(f"K mismatch: a_q has {k}, w_q has {k2}")
+    groups = k // 128
+    if tuple(a_s.shape) != (m, groups) or tuple(w_s.shape) != ((n + 127) // 128, groups):
+        raise ValueError(f"scale shapes {tuple(a_s.shape)}, {tuple(w_s.shape)} do not match M={m}, N={n}, K={k}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a_q.device)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (m, n):
+            raise ValueError(f"out must be [{m}, {n}]")
+    return a_q, w_q, m, n, k, out
+
+
+def gemm(a_q, a_s, w_q, w_s, out=None) -> torch.Tensor:
+    """Block-scaled FP8 GEMM: C[m, n] = sum over K of A[m, k] W[n, k], bf16 [M, N]."""
+    a_q, w_q, m, n, k, out = _gemm_args(a_q, a_s, w_q, w_s, out)
+    with torch.cuda.device(a_q.device):
+        st = lib().fp8bq_gemm(m, n, k, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(out), _stream(a_q))
+    _check("fp8bq_gemm", st)
+    return out
+
+
+def gemm_forced(path: int, a_q, a_s, w_q, w_s, out=None) -> torch.Tensor:
+    """gemm() on a chosen kernel path (PATH_STREAM needs M <= 64)."""
+    a_q, w_q, m, n, k, out = _gemm_args(a_q, a_s, w_q, w_s, out)
+    with torch.cuda.device(a_q.device):
+        st = lib().fp8bq_gemm_forced(int(path), m, n, k, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(out),
+                                     _stream(a_q))
+    _check("fp8bq_gemm_forced", st)
+    return out
+
+
+def gemm_path(m: int, n: int, k: int) -> int:
+    """Kernel path fp8bq_gemm takes for (M, N, K); raises on invalid sizes."""
+    st = lib().fp8bq_gemm_path(int(m), int(n), int(k))
+    if st < 0:
+        raise Fp8bqError("fp8bq_gemm_path", st)
+    return st

@@ -1,0 +1,66 @@
+// Device helpers shared by the fp8bq kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8bq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;       // K entries per scale group
+constexpr float kE4m3Max = 448.f;  // largest finite e4m3fn magnitude
+
+// 16x16 output tile, K = 128, both operands OCP e4m3fn, fresh fp32 result.
+// Operand layout (gfx950 V_MFMA_F32_16X16X128_F8F6F4): lane l supplies row
+// l % 16 of the first operand and column l % 16 of the second; the 32 bytes
+// a lane holds are 32 K-slots determined by (l / 16, byte). The two operands
+// use the same K-slot map, so any consistent placement of a row's 128 bytes
+// gives the exact dot product. Result: lane l, element i holds row
+// 4 * (l / 16) + i, column l % 16. Format code 0 selects e4m3 for both
+// operands; zero scale operands select the unscaled instruction.
+__device__ __forceinline__ v4f mfma_16x16x128_e4m3(const v8i& a, const v8i& b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// Same instruction accumulating into c.
+__device__ __forceinline__ v4f mfma_16x16x128_e4m3_acc(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Two fp32 values to two bf16 (round to nearest even, V_CVT_PK_BF16_F32),
+// packed low = lo, high = hi.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  const v2f f = {lo, hi};
+  const v2bf r = __builtin_convertvector(f, v2bf);
+  return __builtin_bit_cast(unsigned, r);
+}
+
+// Four fp32 values (|x| <= 448) to four e4m3fn codes, round to nearest even,
+// byte i = code of the i-th argument (V_CVT_PK_FP8_F32).
+__device__ __forceinline__ unsigned encode4_e4m3(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return static_cast<unsigned>(w);
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Scale of a group from its amax: IEEE fp32 division by 448, 1.0 for zero.
+__device__ __forceinline__ float group_scale(float amax) { return amax > 0.f ? amax / kE4m3Max : 1.f; }
+
+// Quotient clamped into the e4m3fn range; -0 stays -0.
+__device__ __forceinline__ float scaled_clamped(float x, float s) {
+  return fminf(fmaxf(x / s, -kE4m3Max), kE4m3Max);
+}
+
+}  // namespace fp8bq

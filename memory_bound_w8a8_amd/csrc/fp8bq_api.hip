@@ -1,0 +1,128 @@
+// C ABI of libfp8bq: host-side validation and kernel dispatch. The contract
+// of every entry point is documented in include/fp8bq.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "fp8bq.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 40;  // bound on M*K, N*K, M*N
+constexpr int64_t kStreamMaxM = 64;              // streaming kernel serves 1..64
+constexpr int kMaxDevices = 64;
+
+// Per-device capability cache: 0 = unknown, 1 = gfx950, -1 = not usable.
+std::atomic<int> g_device_ok[kMaxDevices];
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return FP8BQ_ERR_DEVICE;
+  if (dev >= kMaxDevices) return FP8BQ_ERR_DEVICE;
+  int state = g_device_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    state = -1;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0)
+      state = 1;
+    g_device_ok[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? FP8BQ_OK : FP8BQ_ERR_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool product_ok(int64_t a, int64_t b) { return a == 0 || b <= kMaxElems / a; }
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FP8BQ_OK : FP8BQ_ERR_LAUNCH; }
+
+int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales, const void* W_fp8,
+                    const float* W_scales, void* C_bf16) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
+  if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BQ_OK;
+  if (C_bf16 == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(C_bf16, 16)) return FP8BQ_ERR_ALIGN;
+  if (K == 0) return FP8BQ_OK;
+  if (A_fp8 == nullptr || A_scales == nullptr || W_fp8 == nullptr || W_scales == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(A_fp8, 16) || !aligned(W_fp8, 16) || !aligned(A_scales, 4) || !aligned(W_scales, 4))
+    return FP8BQ_ERR_ALIGN;
+  return FP8BQ_OK;
+}
+
+int gemm_path(int64_t M) { return M <= kStreamMaxM ? FP8BQ_PATH_STREAM : FP8BQ_PATH_TILED; }
+
+int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales,
+             const void* W_fp8, const float* W_scales, void* C_bf16, void* stream) {
+  int st = check_gemm_args(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16);
+  if (st != FP8BQ_OK) return st;
+  if (path == FP8BQ_PATH_STREAM && M > kStreamMaxM) return FP8BQ_ERR_SHAPE;
+  if (path != FP8BQ_PATH_STREAM && path != FP8BQ_PATH_TILED) return FP8BQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BQ_OK;
+  st = check_device();
+  if (st != FP8BQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return launch_status(fp8bq::launch_fill_zero_bf16(M * N, C_bf16, s));
+  if (path == FP8BQ_PATH_STREAM)
+    return launch_status(fp8bq::launch_gemm_stream(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s));
+  return launch_status(fp8bq::launch_gemm_tiled(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8bq_quant_act(int64_t M, int64_t K, const void* A_bf16, void* A_fp8, float* A_scales, void* stream) {
+  if (M < 0 || K < 0 || K % 128 != 0 || !product_ok(M, K)) return FP8BQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return FP8BQ_OK;
+  if (A_bf16 == nullptr || A_fp8 == nullptr || A_scales == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(A_bf16, 16) || !aligned(A_fp8, 16) || !aligned(A_scales, 4)) return FP8BQ_ERR_ALIGN;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(fp8bq::launch_quant_act(M, K, A_bf16, A_fp8, A_scales, static_cast<hipStream_t>(stream)));
+}
+
+int fp8bq_quant_weight(int64_t N, int64_t K, const float* W_f32, void* W_fp8, float* W_scales, void* stream) {
+  if (N < 0 || K < 0 || K % 128 != 0 || !product_ok(N, K)) return FP8BQ_ERR_SHAPE;
+  if ((N + 127) / 128 > 65535) return FP8BQ_ERR_SHAPE;  // row blocks form the grid's y dimension
+  if (N == 0 || K == 0) return FP8BQ_OK;
+  if (W_f32 == nullptr || W_fp8 == nullptr || W_scales == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(W_f32, 16) || !aligned(W_fp8, 16) || !aligned(W_scales, 4)) return FP8BQ_ERR_ALIGN;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(fp8bq::launch_quant_weight(N, K, W_f32, W_fp8, W_scales, static_cast<hipStream_t>(stream)));
+}
+
+int fp8bq_gemm(int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales, const void* W_fp8,
+               const float* W_scales, void* C_bf16, void* stream) {
+  if (M < 0) return FP8BQ_ERR_SHAPE;
+  return run_gemm(gemm_path(M), M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
+}
+
+int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales,
+                      const void* W_fp8, const float* W_scales, void* C_bf16, void* stream) {
+  return run_gemm(path, M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
+}
+
+int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
+  if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BQ_PATH_NONE;
+  return gemm_path(M);
+}
+
+const char* fp8bq_status_string(int status) {
+  switch (status) {
+    case FP8BQ_OK: return "ok";
+    case FP8BQ_ERR_NULL: return "null pointer argument";
+    case FP8BQ_ERR_SHAPE: return "invalid size (negative, K % 128 != 0, too large, or path cannot serve M)";
+    case FP8BQ_ERR_ALIGN: return "misaligned pointer (codes/bf16 need 16 B, fp32 scales 4 B)";
+    case FP8BQ_ERR_DEVICE: return "no usable HIP device (gfx950 required)";
+    case FP8BQ_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

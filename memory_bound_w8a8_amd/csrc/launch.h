@@ -1,0 +1,24 @@
+// Host-side launchers of the fp8bq kernels (internal to libfp8bq.so).
+// Arguments are validated by the C-ABI layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bq {
+
+hipError_t launch_quant_act(int64_t m, int64_t k, const void* a, void* aq, float* as, hipStream_t stream);
+hipError_t launch_quant_weight(int64_t n, int64_t k, const float* w, void* wq, float* ws, hipStream_t stream);
+
+// Weight-streaming split-K kernel, 1 <= m <= 64.
+hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
+                              const void* wq, const float* ws, void* c, hipStream_t stream);
+
+// LDS-tiled MFMA kernel, any m >= 1.
+hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
+                             const void* wq, const float* ws, void* c, hipStream_t stream);
+
+// C = 0 (used for K == 0).
+hipError_t launch_fill_zero_bf16(int64_t count, void* c, hipStream_t stream);
+
+}  // namespace fp8bq

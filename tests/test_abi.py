@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports what include/fp8bq.h declares, and
+rejects bad arguments on the host before touching any device (CPU only)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bq.h")
+
+
+@pytest.fixture(scope="module")
+def fp8bq():
+    import memory_bound_w8a8_amd as m
+
+    if not os.path.exists(m.LIB_PATH):
+        from memory_bound_w8a8_amd import build
+
+        build.build()
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:int|const char \*)\s*(fp8bq_\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_declares_the_abi():
+    assert _declared() == {"fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_path",
+                           "fp8bq_gemm_forced", "fp8bq_status_string"}
+
+
+def test_library_exports_every_declared_symbol(fp8bq):
+    raw = ctypes.CDLL(fp8bq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+    assert set(fp8bq.EXPORTS) == _declared()
+
+
+def test_status_strings(fp8bq):
+    L = fp8bq.lib()
+    for st in (0, -1, -2, -3, -4, -5):
+        s = L.fp8bq_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert L.fp8bq_status_string(42).decode() == "unknown status"
+
+
+FAKE = 1 << 20  # an aligned, never-dereferenced address for host-side checks
+
+
+def test_gemm_shape_errors(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    assert L.fp8bq_gemm(-1, 4, 128, p, p, p, p, p, None) == -2
+    assert L.fp8bq_gemm(1, -4, 128, p, p, p, p, p, None) == -2
+    assert L.fp8bq_gemm(1, 4, -128, p, p, p, p, p, None) == -2
+    assert L.fp8bq_gemm(1, 4, 100, p, p, p, p, p, None) == -2
+    assert L.fp8bq_gemm(1 << 21, 1 << 21, 128, p, p, p, p, p, None) == -2  # M*N > 2^40
+    assert L.fp8bq_gemm_forced(1, 65, 4, 128, p, p, p, p, p, None) == -2  # stream path serves M <= 64
+    assert L.fp8bq_gemm_forced(7, 1, 4, 128, p, p, p, p, p, None) == -2  # unknown path
+
+
+def test_gemm_quick_return_and_null_and_alignment(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    assert L.fp8bq_gemm(0, 4, 128, None, None, None, None, None, None) == 0
+    assert L.fp8bq_gemm(4, 0, 128, None, None, None, None, None, None) == 0
+    assert L.fp8bq_gemm(1, 4, 128, None, p, p, p, p, None) == -1
+    assert L.fp8bq_gemm(1, 4, 128, p, None, p, p, p, None) == -1
+    assert L.fp8bq_gemm(1, 4, 128, p, p, None, p, p, None) == -1
+    assert L.fp8bq_gemm(1, 4, 128, p, p, p, None, p, None) == -1
+    assert L.fp8bq_gemm(1, 4, 128, p, p, p, p, None, None) == -1
+    assert L.fp8bq_gemm(1, 4, 128, p + 8, p, p, p, p, None) == -3
+    assert L.fp8bq_gemm(1, 4, 128, p, p + 2, p, p, p, None) == -3
+    assert L.fp8bq_gemm(1, 4, 128, p, p, p + 1, p, p, None) == -3
+    assert L.fp8bq_gemm(1, 4, 128, p, p, p, p + 1, p, None) == -3
+    assert L.fp8bq_gemm(1, 4, 128, p, p, p, p, p + 2, None) == -3
+
+
+def test_quant_errors(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    assert L.fp8bq_quant_act(-1, 128, p, p, p, None) == -2
+    assert L.fp8bq_quant_act(1, 130, p, p, p, None) == -2
+    assert L.fp8bq_quant_act(0, 128, None, None, None, None) == 0
+    assert L.fp8bq_quant_act(1, 128, None, p, p, None) == -1
+    assert L.fp8bq_quant_act(1, 128, p + 2, p, p, None) == -3
+    assert L.fp8bq_quant_act(1, 128, p, p + 4, p, None) == -3
+    assert L.fp8bq_quant_act(1, 128, p, p, p + 1, None) == -3
+    assert L.fp8bq_quant_weight(1, 64, p, p, p, None) == -2
+    assert L.fp8bq_quant_weight(128 * 70000, 128, p, p, p, None) == -2
+    assert L.fp8bq_quant_weight(0, 128, None, None, None, None) == 0
+    assert L.fp8bq_quant_weight(5, 128, p, None, p, None) == -1
+    assert L.fp8bq_quant_weight(5, 128, p + 4, p, p, None) == -3
+
+
+def test_gemm_path_dispatch_by_explicit_m_ranges(fp8bq):
+    L = fp8bq.lib()
+    assert L.fp8bq_gemm_path(0, 17408, 5120) == fp8bq.PATH_NONE
+    for m in list(range(1, 65)):
+        assert L.fp8bq_gemm_path(m, 17408, 5120) == fp8bq.PATH_STREAM, m
+    for m in (65, 128, 2048, 3465, 4096):
+        assert L.fp8bq_gemm_path(m, 17408, 5120) == fp8bq.PATH_TILED, m
+    assert L.fp8bq_gemm_path(1, 17408, 5000) == -2
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device error; a GPU is present")
+def test_device_error_without_gpu(fp8bq):
+    # All arguments valid: the only failure left is the device check, which
+    # must come back as an error rather than a launch.
+    L = fp8bq.lib()
+    p = FAKE
+    assert L.fp8bq_gemm(1, 4, 128, p, p, p, p, p, None) == -4
+    assert L.fp8bq_quant_act(1, 128, p, p, p, None) == -4
+
+
+def test_binding_rejects_cpu_tensors(fp8bq):
+    with pytest.raises(ValueError):
+        fp8bq.quant_act(torch.zeros(1, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fp8bq.gemm(torch.zeros(1, 128, dtype=torch.uint8), torch.zeros(1, 1), torch.zeros(4, 128, dtype=torch.uint8),
+                   torch.zeros(1, 1))

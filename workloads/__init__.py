@@ -17,9 +17,10 @@ pages' shapes replace them:
 * the tiny case (M=1, N=512, K=1024) uses one generator seeded 0, drawing W
   first and then A, with no outliers.
 
-Seeds: W for shape (N, K) comes from ``numpy.random.default_rng([0, N, K])``;
-A for (M, N, K) from ``default_rng([0, N, K, M])``, normals first, outlier
-positions second.
+Seeds: W for shape (N, K) is drawn one 128-row block at a time, block b
+from ``numpy.random.default_rng([0, N, K, b])`` (so a test can rebuild any
+row block without drawing the whole matrix); A for (M, N, K) comes from
+``default_rng([1, N, K, M])``, normals first, outlier positions second.
 """
 
 import numpy as np
@@ -48,15 +49,26 @@ def tiny_inputs():
     return to_bf16(a), w
 
 
+def weight_block(n: int, k: int, b: int) -> np.ndarray:
+    """Rows 128 b .. min(128 b + 128, N) - 1 of weight(n, k)."""
+    rows = min(128, n - 128 * b)
+    if rows <= 0:
+        raise ValueError(f"row block {b} is outside N={n}")
+    rng = np.random.default_rng([0, n, k, b])
+    return (np.float32(0.02) * rng.standard_normal((rows, k), dtype=np.float32)).astype(np.float32)
+
+
 def weight(n: int, k: int) -> np.ndarray:
-    """W fp32 [N, K] = 0.02 * N(0, 1), seeded by the shape."""
-    rng = np.random.default_rng([0, n, k])
-    return (0.02 * rng.standard_normal((n, k), dtype=np.float32)).astype(np.float32)
+    """W fp32 [N, K] = 0.02 * N(0, 1), drawn per 128-row block."""
+    out = np.empty((n, k), dtype=np.float32)
+    for b in range((n + 127) // 128):
+        out[128 * b : 128 * b + 128] = weight_block(n, k, b)
+    return out
 
 
 def activation(m: int, n: int, k: int, outliers: bool = True) -> torch.Tensor:
     """A bf16 [M, K] = N(0, 1) with 0.1 % outliers x20, seeded by (N, K, M)."""
-    rng = np.random.default_rng([0, n, k, m])
+    rng = np.random.default_rng([1, n, k, m])
     a = rng.standard_normal((m, k), dtype=np.float32)
     if outliers and m * k > 0:
         count = max(1, int(round(OUTLIER_FRACTION * m * k)))
