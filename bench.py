@@ -1,0 +1,280 @@
+"""Benchmark of the block-FP8 decode GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: the decode and speculative-verify shapes M = 1..8 on the largest
+logged weight shape N = 17408, K = 5120 (page 2, ownding.com L20 report,
+section 8). One step is one pass of the whole hot path over that workload:
+for every M, quantise the activation (fp8bq_quant_act) and run the
+block-FP8 GEMM (fp8bq_gemm). Inputs are resident in HBM before timing. The
+weights rotate over enough distinct copies (>= 1 GiB) that no call finds its
+89 MB weight in the 256 MB Infinity Cache, so every GEMM reads W from HBM.
+
+Printed: one JSON line with the step throughput (algorithmic bytes per step
+/ step time, GB/s), per-M microseconds per call from HIP events on the
+launch stream, the roofline of the dominant kernel (the GEMM) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import memory_bound_w8a8_amd as fp8bq  # noqa: E402
+import workloads  # noqa: E402
+
+N, K = 17408, 5120
+MS = list(range(1, 9))
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MALL_BYTES = 256 << 20
+METRIC = "block-FP8 GEMM HBM GB/s (% of peak) + us/call, M=1-8, N=17408 K=5120"
+
+
+def gemm_bytes(m, n, k):
+    """Algorithmic bytes of one GEMM call: W codes + W scales + A codes +
+    A scales + C (bf16)."""
+    g = k // 128
+    return n * k + 4 * ((n + 127) // 128) * g + m * k + 4 * m * g + 2 * m * n
+
+
+def quant_bytes(m, k):
+    """Algorithmic bytes of one activation quantisation: bf16 in, codes and
+    fp32 scales out."""
+    return 2 * m * k + m * k + 4 * m * (k // 128)
+
+
+def kernel_source_digest():
+    """Hash of the GEMM kernel sources, to tie stored counter data to code."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "memory_bound_w8a8_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(digest):
+    """HBM traffic per GEMM launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "gemm_stream_decode_M1-8_N17408_K5120_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                key, _, val = ln.partition(":")
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_source_digest") != digest:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Plan:
+    """Device buffers and raw C-ABI launch arguments for one step."""
+
+    def __init__(self, copies, seed=1234):
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream(self.dev)
+        self.lib = fp8bq.lib()
+        g = torch.Generator(device=self.dev)
+        self.w = []
+        for i in range(copies):
+            g.manual_seed(seed + i)
+            w32 = torch.randn((N, K), generator=g, device=self.dev, dtype=torch.float32).mul_(0.02)
+            self.w.append(fp8bq.quant_weight(w32))
+            del w32
+        self.a = {m: workloads.activation(m, N, K).to(self.dev) for m in MS}
+        self.aq = {m: torch.empty((m, K), dtype=torch.uint8, device=self.dev) for m in MS}
+        self.as_ = {m: torch.empty((m, K // 128), dtype=torch.float32, device=self.dev) for m in MS}
+        self.c = {m: torch.empty((m, N), dtype=torch.bfloat16, device=self.dev) for m in MS}
+        self.s = ctypes.c_void_p(self.stream.cuda_stream)
+        self.next_w = 0
+        torch.cuda.synchronize()
+
+    def quant(self, m):
+        st = self.lib.fp8bq_quant_act(m, K, self.a[m].data_ptr(), self.aq[m].data_ptr(), self.as_[m].data_ptr(),
+                                      self.s)
+        if st:
+            raise fp8bq.Fp8bqError("fp8bq_quant_act", st)
+
+    def gemm(self, m):
+        wq, ws = self.w[self.next_w]
+        self.next_w = (self.next_w + 1) % len(self.w)
+        st = self.lib.fp8bq_gemm(m, N, K, self.aq[m].data_ptr(), self.as_[m].data_ptr(), wq.data_ptr(),
+                                 ws.data_ptr(), self.c[m].data_ptr(), self.s)
+        if st:
+            raise fp8bq.Fp8bqError("fp8bq_gemm", st)
+
+    def step(self):
+        for m in MS:
+            self.quant(m)
+            self.gemm(m)
+
+
+def time_kernels(plan, reps):
+    """Average duration of each launch kind, from HIP events on the launch
+    stream around `reps` back-to-back launches (rotating weights)."""
+    out = {}
+    for m in MS:
+        for kind, fn in (("gemm", plan.gemm), ("quant", plan.quant)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            fn(m)
+            e0.record(plan.stream)
+            for _ in range(reps):
+                fn(m)
+            e1.record(plan.stream)
+            e1.synchronize()
+            out[(kind, m)] = e0.elapsed_time(e1) * 1e3 / reps  # us
+    return out
+
+
+def cpu_baseline(budget_s=20.0, rows=4096):
+    """The CPU oracle (numpy, fp64 GEMM) on a bounded sample: quantise the
+    activation and compute the GEMM for M = 1..8 against the first `rows`
+    weight rows of the same workload, repeated until about `budget_s` of CPU
+    work. Reports GB/s of algorithmic bytes, like the GPU figure."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import gemm_ref, quant_act_ref, quant_weight_ref
+
+    cores = len(os.sched_getaffinity(0))
+    cores = min(cores, 16)  # the GPU machine's CPU share
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        blocks = [quant_weight_ref(workloads.weight_block(N, K, b)) for b in range(rows // 128)]
+        w_q = np.concatenate([q for q, _ in blocks])
+        w_s = np.concatenate([s for _, s in blocks])
+        acts = {m: workloads.activation(m, N, K) for m in MS}
+        passes, t_total, bytes_total = 0, 0.0, 0
+        while t_total < budget_s and passes < 20:
+            t0 = time.perf_counter()
+            for m in MS:
+                a_q, a_s = quant_act_ref(acts[m])
+                gemm_ref(a_q, a_s, w_q, w_s)
+            t_total += time.perf_counter() - t0
+            bytes_total += sum(gemm_bytes(m, rows, K) + quant_bytes(m, K) for m in MS)
+            passes += 1
+    return {
+        "value": round(bytes_total / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": used,
+        "kind": "oracle",
+        "sample": f"{passes} pass(es) of quant_act_ref + gemm_ref for M=1..8 on the first {rows} of {N} weight "
+                  f"rows (K={K}); {t_total:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--kernel-reps", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this path has no multi-GPU mode.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w_bytes = N * K
+    copies = max(4, -(-(1 << 30) // w_bytes))  # >= 1 GiB of distinct weights
+    print(f"bench: preparing {copies} weight copies of N={N} K={K} ({copies * w_bytes / 1e9:.2f} GB)",
+          file=sys.stderr, flush=True)
+    plan = Plan(copies)
+
+    for _ in range(args.warmup):
+        plan.step()
+    torch.cuda.synchronize()
+
+    print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(plan.stream)
+    for _ in range(args.steps):
+        plan.step()
+    e1.record(plan.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    kt = time_kernels(plan, args.kernel_reps)
+    step_bytes = sum(gemm_bytes(m, N, K) + quant_bytes(m, K) for m in MS)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    per_m = []
+    for m in MS:
+        us = kt[("gemm", m)]
+        gbs = gemm_bytes(m, N, K) / (us * 1e-6) / 1e9
+        per_m.append({"M": m, "gemm_us": round(us, 3), "gemm_GBps": round(gbs, 1),
+                      "gemm_pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "quant_act_us": round(kt[("quant", m)], 3)})
+    g_bytes = sum(gemm_bytes(m, N, K) for m in MS)
+    g_time = sum(kt[("gemm", m)] for m in MS) * 1e-6
+    achieved = g_bytes / g_time / 1e9
+    digest = kernel_source_digest()
+    traffic = stored_traffic(digest)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode/verify M=1..8 x (N=17408, K=5120): quant_act + block-FP8 gemm per M",
+            "M": MS, "N": N, "K": K, "weight_copies": copies, "step_bytes": step_bytes,
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
+            "parallelism": "single GPU",
+        },
+        "per_m": per_m,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "gemm_rows_kernel (the M=1..8 launches; HIP events around back-to-back launches)",
+        },
+        "wall_s_timed": round(wall, 3),
+        "kernel_source_digest": digest,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

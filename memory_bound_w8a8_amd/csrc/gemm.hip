@@ -1,5 +1,20 @@
 // Kernel instances and launch configuration of the block-FP8 GEMM.
+//
+// Streaming path (M <= 64). The launch shape follows from (N, K) alone:
+//   rows per workgroup R = N / 256 rounded up to a multiple of 4 (one
+//   workgroup per CU; at most 16 * kMaxTiles rows, beyond that more
+//   workgroups), TILES = ceil(R / 16), and with S = 8 waves splitting the
+//   K / 128 groups, GMAX = ceil(groups / 8).
+// M only selects the token tile (16 or 32 tokens per MFMA column block), so
+// every M inside a tile runs the same instruction stream. Each (TILES, GMAX)
+// pair has its own compiled instance, looked up exactly; shapes outside the
+// table (very large K) run the generic streaming kernel, which handles any
+// size with runtime loops.
+#include <array>
+#include <utility>
+
 #include "device_common.h"
+#include "gemm_rows.h"
 #include "gemm_stream.h"
 #include "gemm_tiled.h"
 #include "launch.h"
@@ -8,12 +23,54 @@ namespace fp8bq {
 
 namespace {
 
+constexpr int kNumCUs = 256;   // MI355X
+constexpr int kRowsWaves = 8;  // waves per workgroup in the row-range kernel
+constexpr int kMaxTiles = 5;
+constexpr int kMaxGroupsPerWave = 9;
+
+struct GemmArgs {
+  int64_t m, n, k;
+  const void* aq;
+  const float* as;
+  const void* wq;
+  const float* ws;
+  void* c;
+  hipStream_t stream;
+};
+
+using Launch = hipError_t (*)(const GemmArgs&, int64_t rows_per_wg);
+
+template <int MT, int TILES, int GMAX>
+hipError_t rows_instance(const GemmArgs& a, int64_t rows_per_wg) {
+  // chunks of weight loads kept in flight per wave (fewer where the held
+  // activation operand of a 32-token tile already takes most registers)
+  constexpr int PD = MT == 16 ? 6 : (GMAX <= 6 ? 4 : 2);
+  const unsigned grid = static_cast<unsigned>((a.n + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((gemm_rows_kernel<MT, kRowsWaves, GMAX, TILES, PD>), dim3(grid), dim3(64 * kRowsWaves), 0,
+                     a.stream, static_cast<int>(a.m), a.n, a.k, rows_per_wg,
+                     static_cast<const unsigned char*>(a.aq), a.as, static_cast<const unsigned char*>(a.wq), a.ws,
+                     static_cast<unsigned short*>(a.c));
+  return hipGetLastError();
+}
+
+template <int MT, int TILES, int... G>
+constexpr std::array<Launch, sizeof...(G)> rows_row(std::integer_sequence<int, G...>) {
+  return {&rows_instance<MT, TILES, G + 1>...};
+}
+
+template <int MT, int... T>
+constexpr std::array<std::array<Launch, kMaxGroupsPerWave>, sizeof...(T)> rows_table(std::integer_sequence<int, T...>) {
+  return {rows_row<MT, T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
+}
+
+constexpr auto kRows16 = rows_table<16>(std::make_integer_sequence<int, kMaxTiles>{});
+constexpr auto kRows32 = rows_table<32>(std::make_integer_sequence<int, kMaxTiles>{});
+
 template <int MT, int R, int S, int U>
-hipError_t stream_instance(int64_t m, int64_t n, int64_t k, const void* aq, const float* as, const void* wq,
-                           const float* ws, void* c, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_stream_kernel<MT, R, S, U>), dim3(stream_grid<R>(n)), dim3(64 * S), 0, stream,
-                     static_cast<int>(m), n, k, static_cast<const unsigned char*>(aq), as,
-                     static_cast<const unsigned char*>(wq), ws, static_cast<unsigned short*>(c));
+hipError_t stream_instance(const GemmArgs& a) {
+  hipLaunchKernelGGL((gemm_stream_kernel<MT, R, S, U>), dim3(stream_grid<R>(a.n)), dim3(64 * S), 0, a.stream,
+                     static_cast<int>(a.m), a.n, a.k, static_cast<const unsigned char*>(a.aq), a.as,
+                     static_cast<const unsigned char*>(a.wq), a.ws, static_cast<unsigned short*>(a.c));
   return hipGetLastError();
 }
 
@@ -24,14 +81,37 @@ __global__ void fill_zero_kernel(unsigned short* __restrict__ c, int64_t count) 
 
 }  // namespace
 
-// M-range dispatch of the streaming kernel: the token tile is the smallest
-// MFMA multiple covering M, so every M in a range runs the same instruction
-// stream (cost flat in M within the range).
+// Row-range launch shape for (M, N, K): rows per workgroup, tiles, groups
+// per wave. Returns false when the shape is outside the compiled table.
+bool rows_shape(int64_t m, int64_t n, int64_t k, int64_t* rows_per_wg, int* tiles, int* gmax) {
+  const int64_t groups = k / kGroup;
+  const int64_t g = (groups + kRowsWaves - 1) / kRowsWaves;
+  if (g < 1 || g > kMaxGroupsPerWave) return false;
+  int64_t r = (n + kNumCUs - 1) / kNumCUs;
+  r = (r + 3) / 4 * 4;
+  // A 32-token tile holding 7+ groups of activation operand leaves registers
+  // for at most two row tiles' bookkeeping: use more, smaller workgroups.
+  const int64_t max_rows = (m > 16 && g >= 7) ? 32 : 16 * kMaxTiles;
+  if (r > max_rows) r = max_rows;
+  *rows_per_wg = r;
+  *tiles = static_cast<int>((r + 15) / 16);
+  *gmax = static_cast<int>(g);
+  return true;
+}
+
 hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                               const void* wq, const float* ws, void* c, hipStream_t stream) {
-  if (m <= 16) return stream_instance<16, 1, 8, 4>(m, n, k, aq, as, wq, ws, c, stream);
-  if (m <= 32) return stream_instance<32, 1, 8, 4>(m, n, k, aq, as, wq, ws, c, stream);
-  return stream_instance<64, 1, 8, 2>(m, n, k, aq, as, wq, ws, c, stream);
+  const GemmArgs a{m, n, k, aq, as, wq, ws, c, stream};
+  int64_t rows_per_wg;
+  int tiles, gmax;
+  if (m <= 32 && rows_shape(m, n, k, &rows_per_wg, &tiles, &gmax)) {
+    const auto& table = m <= 16 ? kRows16 : kRows32;
+    return table[tiles - 1][gmax - 1](a, rows_per_wg);
+  }
+  // Generic streaming kernel: any N and K, 16-row slabs, runtime K loop.
+  if (m <= 16) return stream_instance<16, 1, 8, 5>(a);
+  if (m <= 32) return stream_instance<32, 1, 8, 4>(a);
+  return stream_instance<64, 1, 8, 2>(a);
 }
 
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
@@ -40,9 +120,8 @@ hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, co
   const int64_t n_tiles = (n + BN - 1) / BN;
   const int64_t m_tiles = (m + BM - 1) / BM;
   hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN>), dim3(static_cast<unsigned>(n_tiles * m_tiles)), dim3(256), 0,
-                     stream, m, n, k,
-                     static_cast<const unsigned char*>(aq), as, static_cast<const unsigned char*>(wq), ws,
-                     static_cast<unsigned short*>(c));
+                     stream, m, n, k, static_cast<const unsigned char*>(aq), as,
+                     static_cast<const unsigned char*>(wq), ws, static_cast<unsigned short*>(c));
   return hipGetLastError();
 }
 

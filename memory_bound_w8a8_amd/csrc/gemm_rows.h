@@ -1,0 +1,210 @@
+// Weight-streaming split-K block-FP8 GEMM with balanced row ranges, gfx950.
+//
+// At M <= 64 the op reads every weight byte once and is bound by HBM (page 1,
+// SmartX blog, section "operator optimisation": the weight-reading matmuls
+// take about 89% of a decode step and sit near the bandwidth floor; page 1,
+// same section: a library's poor kernel choice at M = 2..7 cost 8.8x, so the
+// cost here must not depend on M within a token tile). What decides the
+// achieved bandwidth is (a) that every CU streams the same number of bytes,
+// (b) that every load instruction reads whole 128-byte lines, and (c) that
+// each wave keeps loads in flight without ever draining its queue.
+//
+// Decomposition. One workgroup per CU (grid = ceil(N / R)). Workgroup w owns
+// rows [w R, min(w R + R, N)) of W, R a multiple of 4 that spreads N evenly
+// (17408 / 256 = 68 rows), walked as TILES 16-row MFMA tiles. Its S waves
+// split the K/128 scale groups into contiguous ranges of at most GMAX groups
+// (split-K). A wave's work is TILES x GMAX "chunks" of 16 rows x 128 bytes.
+//
+// Loads. For a chunk, load instruction j (j = 0, 1) reads rows 8 j .. 8 j + 7
+// of the tile and the whole 128-byte group of each (lane l: row 8 j + l / 8,
+// 16-byte piece l % 8): 8 full lines per instruction, non-temporal. Rows past
+// the range are clamped onto the range's last row and groups past the wave's
+// range onto its last group (scale forced to 0), so the code has no branches:
+// every wave runs the same straight-line load/compute sequence and the
+// compiler can keep the next PD chunks' loads in flight while computing.
+//
+// Transpose. The MFMA wants lane l to hold 32 bytes of tile row l % 16
+// (16 bytes at 16 (l / 16) and 16 bytes at 64 + 16 (l / 16) of the group),
+// with the activation operand (token l % 16) in the same byte order. A wave
+// writes its chunk to a private LDS slot, piece c of row r at index
+// 8 r + (c ^ (r & 7)) (the XOR makes both the 8-lane write passes and the
+// 8-lane read passes hit 8 distinct 16-byte bank groups), and reads it back
+// in MFMA order. LDS operations of one wave execute in order, so no barrier
+// is needed between the write and the read.
+//
+// Math. One 16x16x128 FP8 MFMA per chunk and 16-token tile gives the 128-long
+// dot products of 16 rows x 16 tokens. Lane l's result covers rows
+// 4 (l / 16) .. +3: an aligned quad that never straddles a 128-row weight
+// block, so acc += (A_scale[m, g] * W_scale[quad / 128, g]) * mfma in fp32.
+//
+// Reduction. After a tile, each wave parks its fp32 16 x MT partial in LDS;
+// at the end the S partials of every tile are summed in wave order 0..S-1
+// (deterministic, no atomics), rounded to bf16 (RNE) and stored, 4
+// consecutive outputs (8 bytes) per lane.
+#pragma once
+
+#include "device_common.h"
+
+namespace fp8bq {
+
+template <int MT, int S, int GMAX, int TILES, int PD>
+struct RowsKernel {
+  static constexpr int kMS = MT / 16;        // 16-token tiles
+  static constexpr int kChunks = TILES * GMAX;
+  static constexpr int kRing = PD + 1;       // chunk register buffers
+  static constexpr int kStageSlots = 2;      // LDS transpose slots per wave
+  static constexpr int kLdsBytes = S * kStageSlots * 2048 + S * TILES * kMS * 1024;
+};
+
+template <int MT, int S, int GMAX, int TILES, int PD>
+__global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n, int64_t k, int64_t rows_per_wg,
+                                                           const unsigned char* __restrict__ aq,
+                                                           const float* __restrict__ as,
+                                                           const unsigned char* __restrict__ wq,
+                                                           const float* __restrict__ ws,
+                                                           unsigned short* __restrict__ c) {
+  using KC = RowsKernel<MT, S, GMAX, TILES, PD>;
+  constexpr int MS = KC::kMS;
+  constexpr int CH = KC::kChunks;
+  constexpr int RING = KC::kRing;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lrow = lane & 15;
+  const int quarter = lane >> 4;
+  const int groups = static_cast<int>(k >> 7);
+
+  const int64_t r_begin = static_cast<int64_t>(blockIdx.x) * rows_per_wg;
+  int64_t r_end = r_begin + rows_per_wg;
+  r_end = r_end < n ? r_end : n;
+  const int64_t r_last = r_end - 1;  // the grid never holds an empty range
+
+  // This wave's contiguous range of K groups (gcnt may be < GMAX, even 0).
+  const int per = groups / S;
+  const int rem = groups - per * S;
+  const int gbeg = wave * per + (wave < rem ? wave : rem);
+  const int gcnt = per + (wave < rem ? 1 : 0);
+  const int glast = gcnt > 0 ? gbeg + gcnt - 1 : 0;
+
+  __shared__ v4u stage[S][KC::kStageSlots][128];
+  __shared__ v4f red[S][TILES][MS][64];
+
+  // Activation operand and scales of this wave's groups, same for all tiles.
+  v8i bv[GMAX][MS];
+  float sa[GMAX][MS];
+#pragma unroll
+  for (int s = 0; s < MS; ++s) {
+    const int m = 16 * s + lrow;
+    const bool mval = m < m_rows;
+    const int mc = mval ? m : m_rows - 1;
+    const unsigned char* ap = aq + static_cast<int64_t>(mc) * k + quarter * 16;
+    const float* sap = as + static_cast<int64_t>(mc) * groups;
+#pragma unroll
+    for (int u = 0; u < GMAX; ++u) {
+      const bool live = u < gcnt;
+      const int g = live ? gbeg + u : glast;
+      const int64_t off = static_cast<int64_t>(g) * kGroup;
+      const v4u lo = *reinterpret_cast<const v4u*>(ap + off);
+      const v4u hi = *reinterpret_cast<const v4u*>(ap + off + 64);
+      bv[u][s] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      const float scale = sap[g];
+      sa[u][s] = (live && mval) ? scale : 0.f;
+    }
+  }
+
+  // Per-lane load bases: rows 8 j + lane / 8 of each tile, piece lane % 8.
+  const int lr8 = lane >> 3;
+  const int piece = lane & 7;
+
+  v8i wv[RING];
+  float sw[RING];
+
+  auto load_chunk = [&](int ci, int slot) {
+    const int t = ci / GMAX;
+    const int u = ci - t * GMAX;
+    const int g = u < gcnt ? gbeg + u : glast;
+    const int64_t off = static_cast<int64_t>(g) * kGroup + piece * 16;
+    int64_t row0 = r_begin + 16 * t + lr8;
+    int64_t row1 = row0 + 8;
+    row0 = row0 < r_end ? row0 : r_last;
+    row1 = row1 < r_end ? row1 : r_last;
+    const v4u lo = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wq + row0 * k + off));
+    const v4u hi = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wq + row1 * k + off));
+    wv[slot] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    int64_t quad = r_begin + 16 * t + 4 * quarter;
+    quad = quad < r_end ? quad : r_last;
+    sw[slot] = ws[(quad >> 7) * groups + g];
+  };
+
+  // Pieces this lane loaded (rows lr8 and lr8 + 8, piece `piece`) -> the
+  // MFMA operand of row lrow (pieces quarter and quarter + 4).
+  auto transpose = [&](const v8i& raw, int st) -> v8i {
+    v4u* slot = stage[wave][st];
+    slot[8 * lr8 + (piece ^ lr8)] = v4u{(unsigned)raw[0], (unsigned)raw[1], (unsigned)raw[2], (unsigned)raw[3]};
+    slot[8 * (lr8 + 8) + (piece ^ lr8)] = v4u{(unsigned)raw[4], (unsigned)raw[5], (unsigned)raw[6], (unsigned)raw[7]};
+    __builtin_amdgcn_wave_barrier();
+    const int x = lrow & 7;
+    const v4u lo = slot[8 * lrow + (quarter ^ x)];
+    const v4u hi = slot[8 * lrow + ((quarter + 4) ^ x)];
+    __builtin_amdgcn_wave_barrier();
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  v4f acc[MS];
+#pragma unroll
+  for (int ci = 0; ci < PD && ci < CH; ++ci) load_chunk(ci, ci % RING);
+#pragma unroll
+  for (int ci = 0; ci < CH; ++ci) {
+    const int t = ci / GMAX;
+    const int u = ci - t * GMAX;
+    if (ci + PD < CH) load_chunk(ci + PD, (ci + PD) % RING);
+    if (u == 0) {
+#pragma unroll
+      for (int s = 0; s < MS; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    const v8i wop = transpose(wv[ci % RING], ci & 1);
+#pragma unroll
+    for (int s = 0; s < MS; ++s) {
+      const v4f p = mfma_16x16x128_e4m3(wop, bv[u][s]);
+      const float sc = sa[u][s] * sw[ci % RING];
+      acc[s][0] = fmaf(sc, p[0], acc[s][0]);
+      acc[s][1] = fmaf(sc, p[1], acc[s][1]);
+      acc[s][2] = fmaf(sc, p[2], acc[s][2]);
+      acc[s][3] = fmaf(sc, p[3], acc[s][3]);
+    }
+    if (u == GMAX - 1) {
+#pragma unroll
+      for (int s = 0; s < MS; ++s) red[wave][t][s][lane] = acc[s];
+    }
+  }
+  __syncthreads();
+
+  // Sum the S partials of every (tile, token tile) and store.
+#pragma unroll
+  for (int item0 = 0; item0 < TILES * MS; item0 += S) {
+    const int item = item0 + wave;
+    if (item < TILES * MS) {
+      const int t = item / MS;
+      const int s = item - t * MS;
+      v4f sum = red[0][t][s][lane];
+#pragma unroll
+      for (int w = 1; w < S; ++w) sum += red[w][t][s][lane];
+      const int m = 16 * s + lrow;
+      const int64_t col = r_begin + 16 * t + 4 * quarter;  // first of 4 consecutive outputs
+      if (m < m_rows && col < r_end) {
+        unsigned short* dst = c + static_cast<int64_t>(m) * n + col;
+        if ((n & 3) == 0 && col + 3 < r_end) {
+          v2u packed;
+          packed[0] = pack_bf16x2(sum[0], sum[1]);
+          packed[1] = pack_bf16x2(sum[2], sum[3]);
+          *reinterpret_cast<v2u*>(dst) = packed;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (col + i < r_end) dst[i] = static_cast<unsigned short>(pack_bf16x2(sum[i], 0.f) & 0xffffu);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace fp8bq

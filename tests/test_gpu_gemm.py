@@ -59,6 +59,30 @@ def test_odd_shapes(m, n, k):
     assert_gemm_close(c, gemm_ref(a_q, a_s, w_q, w_s), what=f"M={m} N={n} K={k}")
 
 
+# Shapes that walk the streaming kernel's instance table: rows per workgroup
+# -> 16-row tiles 1..5, K groups per wave 1..9, a K past the table (generic
+# kernel), N not a multiple of 4, and workgroups whose last tile is short.
+TABLE_SHAPES = [(1000, 9216), (12800, 1024), (20000, 2304), (4100, 5120), (5000, 9344), (300, 8704),
+                (1026, 256), (7, 1280), (2999, 3072)]
+
+
+@pytest.mark.parametrize("n,k", TABLE_SHAPES)
+@pytest.mark.parametrize("m", [1, 3, 8, 16, 17, 32])
+def test_streaming_instance_table(m, n, k):
+    a = workloads.activation(m, n, k)
+    a_q, a_s = quant_act_ref(a)
+    w_q, w_s = quant_weight_ref(workloads.weight(n, k))
+    c = _gpu_gemm(a_q, a_s, w_q, w_s)
+    if n * k <= 12_000_000:
+        assert_gemm_close(c, gemm_ref(a_q, a_s, w_q, w_s), what=f"M={m} N={n} K={k}")
+    else:
+        rng = np.random.default_rng([m, n, k])
+        rows = rng.integers(0, m, 3000)
+        cols = np.concatenate([rng.integers(0, n, 2000), np.arange(n - 1000, n)])
+        ref = gemm_ref_at(a_q, a_s, w_q, w_s, rows, cols)
+        assert_gemm_close(c[rows, cols], ref, what=f"M={m} N={n} K={k} (sampled)")
+
+
 def _integer_problem(m, n, k, vmax, scales, seed):
     rng = np.random.default_rng(seed)
     vals = np.arange(-vmax, vmax + 1, dtype=np.float32)
