@@ -55,10 +55,12 @@ def quant_bytes(m, k):
 
 
 def kernel_source_digest():
-    """Hash of the GEMM kernel sources, to tie stored counter data to code."""
+    """Hash of the sources that define the dominant kernel (the row-range
+    streaming GEMM and its launch configuration), to tie stored counter data
+    to the code it was taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "memory_bound_w8a8_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in ("device_common.h", "gemm_rows.h", "gemm.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -67,7 +69,7 @@ def kernel_source_digest():
 def stored_traffic(digest):
     """HBM traffic per GEMM launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "gemm_stream_decode_M1-8_N17408_K5120_pmc.txt")
+    path = os.path.join(ROOT, "profiles", "gemm_rows_decode_M1-8_N17408_K5120_pmc.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -187,6 +189,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--kernel-reps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="first run one plain device copy of this many MiB (a dispatch of known traffic for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -197,6 +202,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibration_copy_mb > 0:
+        nbytes = args.calibration_copy_mb << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
+        del src, dst
 
     w_bytes = N * K
     copies = max(4, -(-(1 << 30) // w_bytes))  # >= 1 GiB of distinct weights

@@ -1,7 +1,7 @@
 // LDS-tiled FP8 MFMA block-scaled GEMM for large M (batches, prefill),
 // gfx950.
 //
-// At M in the thousands (page 2, ownding.com L20 report, section 5: a
+// At M in the thousands (page 2, ownding.com L20 report, section 4.2: a
 // 3,465-token prompt; section 8: prefill forced onto an M=1 config regressed)
 // the op is a dense contraction well above the FP8 ridge, so it runs on the
 // matrix cores. A workgroup of 4 waves computes a BM x BN tile of C (tokens x

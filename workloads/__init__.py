@@ -5,7 +5,7 @@ it contains none of the quantisation or GEMM arithmetic. Both the CPU oracle
 tests and the HIP-path tests and benchmark take their inputs from here.
 
 The pages measure real Qwen3.8-27B-FP8 weights on ShareGPT prompts (page 1,
-section "test background"), a 3,465-token prompt (page 2, section 5) and
+section "test background"), a 3,465-token prompt (page 2, section 4.2) and
 256-token prompts (page 3, section 2.3). None of that data is available, and
 the GEMM's cost does not depend on the values, so Gaussian stand-ins with the
 pages' shapes replace them:
@@ -29,7 +29,7 @@ import torch
 # The five (N, K) shapes logged in page 2 (ownding.com L20 report), section 8.
 SHAPES = [(17408, 5120), (5120, 3072), (5120, 8704), (7168, 5120), (8192, 5120)]
 TINY = (1, 512, 1024)  # (M, N, K)
-PREFILL_M = 3465  # prompt length of page 2's test protocol (section 5)
+PREFILL_M = 3465  # prompt length of page 2's output test (section 4.2)
 PREFILL_SHAPES = [(17408, 5120), (5120, 8704)]
 OUTLIER_FRACTION = 0.001
 OUTLIER_FACTOR = 20.0
