@@ -99,8 +99,9 @@ int fp8bq_quant_weight(int64_t N, int64_t K, const float *W_f32, void *W_fp8, fl
  * definition; results agree within fp32 accumulation plus bf16 rounding.
  * Two identical calls give bitwise-identical C (no atomics).
  * K == 0 writes zeros. Errors: NULL pointer; negative size; K % 128 != 0;
- * M*K, N*K or M*N > 2^40; code/bf16 pointers not 16-B aligned, scale
- * pointers not 4-B aligned; device not gfx950.
+ * M*K, N*K or M*N > 2^40; M > 64 with K >= 2^24 (the tiled kernel's limit);
+ * code/bf16 pointers not 16-B aligned, scale pointers not 4-B aligned;
+ * device not gfx950.
  */
 int fp8bq_gemm(int64_t M, int64_t N, int64_t K, const void *A_fp8, const float *A_scales,
                const void *W_fp8, const float *W_scales, void *C_bf16, void *stream);

@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep the compiler from forming packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the per-group scale FMAs read them
+    # directly instead of copying each out of an accumulation register
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

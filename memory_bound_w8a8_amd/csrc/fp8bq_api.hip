@@ -12,6 +12,7 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // bound on M*K, N*K, M*N
 constexpr int64_t kStreamMaxM = 64;              // streaming kernel serves 1..64
+constexpr int64_t kTiledMaxK = int64_t(1) << 24; // tiled kernel: 32-bit offsets within a 256-row tile
 constexpr int kMaxDevices = 64;
 
 // Per-device capability cache: 0 = unknown, 1 = gfx950, -1 = not usable.
@@ -59,6 +60,7 @@ int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const
   int st = check_gemm_args(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16);
   if (st != FP8BQ_OK) return st;
   if (path == FP8BQ_PATH_STREAM && M > kStreamMaxM) return FP8BQ_ERR_SHAPE;
+  if (path == FP8BQ_PATH_TILED && K >= kTiledMaxK) return FP8BQ_ERR_SHAPE;
   if (path != FP8BQ_PATH_STREAM && path != FP8BQ_PATH_TILED) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_OK;
   st = check_device();

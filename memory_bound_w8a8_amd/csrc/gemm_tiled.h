@@ -3,169 +3,324 @@
 //
 // At M in the thousands (page 2, ownding.com L20 report, section 4.2: a
 // 3,465-token prompt; section 8: prefill forced onto an M=1 config regressed)
-// the op is a dense contraction well above the FP8 ridge, so it runs on the
-// matrix cores. A workgroup of 4 waves computes a BM x BN tile of C (tokens x
-// weight rows) and walks K one 128-wide scale group at a time:
-//   1. the group's A tile (BM x 128 codes) and W tile (BN x 128 codes) are
-//      copied global -> registers -> LDS, double-buffered so the next
-//      group's copy overlaps this group's MFMAs;
-//   2. each wave multiplies its (BN/2) x (BM/2) sub-tile with 16x16x128 FP8
-//      MFMAs into fresh fp32 accumulators (one instruction per 16x16 tile per
-//      group, weight rows as the first operand);
-//   3. the fresh result is scaled by A_scale[m, g] * W_scale[n / 128, g] and
-//      added to the running fp32 tile (BN = 128 keeps one weight block per
-//      tile, so the weight scale is uniform over the workgroup).
-// LDS rows are padded from 128 to 144 bytes so that the 16-byte operand
-// reads of 8 consecutive lanes (8 different rows, same column) hit 32
-// distinct banks. Rows past M or N are clamped onto the last valid row for
-// loading and masked at the store.
+// the op is a dense contraction far above the FP8 ridge, so it runs on the
+// matrix cores at the largest register tile that fits.
+//
+// Tiling. A workgroup of WM x WN waves computes a BM x BN tile of C (tokens x
+// weight rows); each wave owns a (BM / WM) x (BN / WN) sub-tile held in fp32
+// registers. K is walked one 128-wide scale group per step:
+//   1. the step's A slice (BM x 128 codes), W slice (BN x 128 codes) and the
+//      BM activation scales are copied global -> LDS with direct-to-LDS loads
+//      (no registers), double-buffered: step g + 1 is in flight while step g
+//      computes;
+//   2. each wave reads its W fragments once per step and streams its token
+//      fragments; one 16x16x128 FP8 MFMA per 16 x 16 sub-tile gives the
+//      group's exact products into a fresh accumulator (weight rows first
+//      operand, tokens second);
+//   3. acc += (A_scale[m, g] * W_scale[n / 128, g]) * mfma in fp32: one FMA
+//      per output per group, which the VALU issues while the matrix core runs
+//      the next MFMAs (4 FMAs per 32-cycle MFMA).
+// LDS layout: each tile row is 128 bytes, its 16-byte chunk c stored at
+// position c ^ (row & 7). A direct-to-LDS load writes lane i's 16 bytes at
+// base + 16 i, so lane i of the load covering rows 8 q .. 8 q + 7 fetches
+// chunk (i % 8) ^ (row & 7) of row 8 q + i / 8; the fragment reads (8 lanes =
+// 8 rows, one chunk each) then hit 8 distinct 16-byte bank groups.
+// Workgroups are mapped to tiles XCD by XCD (hardware places workgroup b on
+// XCD b % 8): each XCD gets a contiguous run of the tile order, which walks
+// bands of 8 token tiles with the token tile fastest, so the ~32 tiles
+// resident on one XCD form a compact block sharing A and W slices in L2.
+// Rows past M or N are clamped onto the last valid row for loading and masked
+// at the store.
 #pragma once
+
+#include <type_traits>
 
 #include "device_common.h"
 
 namespace fp8bq {
 
-constexpr int kTileLdsStride = 144;  // bytes per LDS row (128 + 16 pad)
+typedef __attribute__((address_space(3))) const void lds_void;
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(int64_t m_rows, int64_t n, int64_t k,
-                                                         const unsigned char* __restrict__ aq,
-                                                         const float* __restrict__ as,
-                                                         const unsigned char* __restrict__ wq,
-                                                         const float* __restrict__ ws,
-                                                         unsigned short* __restrict__ c) {
-  static_assert(BN == 128, "one weight scale block per tile");
-  static_assert(BM % 32 == 0 && BM <= 128, "BM");
-  constexpr int WM = BM / 2;  // tokens per wave
-  constexpr int WN = BN / 2;  // weight rows per wave
-  constexpr int TM = WM / 16; // 16-token sub-tiles per wave
-  constexpr int TN = WN / 16; // 16-row sub-tiles per wave
-  constexpr int A_LOADS = BM * 8 / 256;  // 16-byte chunks per thread for A
-  constexpr int W_LOADS = BN * 8 / 256;
+// Direct global -> LDS copies (lane i's bytes land at base + size * i; the
+// LDS base goes through M0 and must be uniform across the wave). Issued as
+// inline assembly so that the compiler does not track them: it cannot tell
+// which stage a copy writes and would otherwise wait for every copy in
+// flight before each LDS read. The kernel orders them itself (explicit
+// vmcnt wait + barrier before a stage is read or rewritten).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds_a[2][BM * kTileLdsStride];
-  __shared__ __attribute__((aligned(16))) unsigned char lds_w[2][BN * kTileLdsStride];
+template <int BM, int BN, int WM, int WN, int STAGES>
+struct TiledKernel {
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kTM = BM / WM;  // tokens per wave
+  static constexpr int kTN = BN / WN;  // weight rows per wave
+  static constexpr int kJ = kTM / 16;  // token sub-tiles per wave
+  static constexpr int kI = kTN / 16;  // weight-row sub-tiles per wave
+  // A codes, W codes, then one 64-token slot of activation scales per wave
+  // (waves past BM / 64 load a duplicate that is never read)
+  static constexpr int kStageBytes = (BM + BN) * 128 + kWaves * 64 * 4;
+  static constexpr int kLdsBytes = STAGES * kStageBytes;
+  // direct-to-LDS loads one wave issues per K step
+  static constexpr int kLoadsPerWave = BM / 8 / kWaves + BN / 8 / kWaves + 1;
+};
 
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding, then barrier the workgroup. Written out because
+// __syncthreads() carries a workgroup memory fence, which would also wait
+// for the tile copies still in flight (direct-to-LDS loads count as LDS
+// stores) and so drain the pipeline at every step. The memory clobber keeps
+// the compiler from moving memory operations across it. Ordering this
+// relies on: every LDS read of a step is consumed by that step's MFMAs, so
+// it has completed before the barrier.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Tile index of workgroup b: XCD-contiguous runs of the tile space.
+__device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t tiles) {
+  const int64_t x = b & 7, s = b >> 3;
+  const int64_t per = tiles >> 3, rem = tiles & 7;
+  const int64_t start = x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per;
+  return start + s;
+}
+
+// Tile t -> (token tile, weight tile) in bands of `band` token tiles: inside
+// a band the token tile runs fastest, so any run of consecutive tiles covers
+// a compact block (e.g. 32 tiles = 8 token x 4 weight tiles) whose A and W
+// slices are shared through L2. A last, narrower band takes the remainder.
+__device__ __forceinline__ void band_tile(int64_t t, int64_t m_tiles, int64_t n_tiles, int64_t band, int64_t* tm,
+                                          int64_t* tn) {
+  const int64_t full_bands = m_tiles / band;
+  const int64_t in_full = full_bands * band * n_tiles;
+  if (t < in_full) {
+    const int64_t b = t / (band * n_tiles);
+    const int64_t w = t - b * band * n_tiles;
+    *tn = w / band;
+    *tm = b * band + (w - *tn * band);
+  } else {
+    const int64_t last = m_tiles - full_bands * band;  // > 0 whenever this branch runs
+    const int64_t w = t - in_full;
+    *tn = w / last;
+    *tm = full_bands * band + (w - *tn * last);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows, int64_t n, int64_t k,
+                                                                  const unsigned char* __restrict__ aq,
+                                                                  const float* __restrict__ as,
+                                                                  const unsigned char* __restrict__ wq,
+                                                                  const float* __restrict__ ws,
+                                                                  unsigned short* __restrict__ c) {
+  using KC = TiledKernel<BM, BN, WM, WN, STAGES>;
+  constexpr int WAVES = KC::kWaves;
+  constexpr int TM = KC::kTM, TN = KC::kTN, J = KC::kJ, I = KC::kI;
+  static_assert(TN <= 128 && 128 % TN == 0, "a wave's weight rows must sit in one 128-row scale block");
+  static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "8-row load chunks spread over the waves");
+  static_assert(BM % 64 == 0 && BM <= 64 * WAVES, "scales: one dword per token, 64 tokens per wave");
+  static_assert(STAGES == 2 || STAGES == 3, "STAGES");
+
+  // One LDS object per stage: the compiler then sees that the copies into
+  // one stage cannot alias the fragment reads of another, and does not wait
+  // for the in-flight copies before every read.
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[KC::kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[KC::kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds2[STAGES > 2 ? KC::kStageBytes : 16];
+
+  const int lane = threadIdx.x & 63;
+  // wave index as a provably uniform value: per-wave pointers (the weight
+  // scale row) then live in scalar registers and their loads go through the
+  // scalar cache, outside the in-order vector-memory counter that tracks the
+  // in-flight tile copies
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lrow = lane & 15;
   const int quarter = lane >> 4;
-  const int wave_n = wave & 1;   // which half of the BN rows
-  const int wave_m = wave >> 1;  // which half of the BM tokens
+  const int wave_m = wave % WM;
+  const int wave_n = wave / WM;
   const int64_t groups = k >> 7;
-  // Linear tile id -> (weight-row tile, token tile), token tile fastest so
-  // that consecutive workgroups share one weight tile.
+
   const int64_t m_tiles = (m_rows + BM - 1) / BM;
-  const int64_t tile = blockIdx.x;
-  const int64_t n0 = (tile / m_tiles) * BN;
-  const int64_t m0 = (tile % m_tiles) * BM;
+  const int64_t n_tiles = (n + BN - 1) / BN;
+  int64_t tm, tn;
+  band_tile(xcd_tile(blockIdx.x, m_tiles * n_tiles), m_tiles, n_tiles, 8, &tm, &tn);
+  const int64_t m0 = tm * BM;
+  const int64_t n0 = tn * BN;
 
-  // Global -> LDS copy assignment: thread t moves 16-byte chunk t % 8 of
-  // rows t / 8 + 32 j.
-  const int chunk = t & 7;
-  const unsigned char* a_src[A_LOADS];
-  const unsigned char* w_src[W_LOADS];
+  // ---- global -> LDS copy plan (per wave: chunks of 8 rows x 128 bytes) ----
+  constexpr int A_CHUNKS = BM / 8 / WAVES;  // per wave
+  constexpr int W_CHUNKS = BN / 8 / WAVES;
+  const int cr = lane >> 3;                 // row within the 8-row chunk
+  // Per-lane 32-bit offsets from the tile's first row (which sits in scalar
+  // registers); a tile spans at most 256 rows of K bytes.
+  const unsigned char* a_base = aq + m0 * k;
+  const unsigned char* w_base = wq + n0 * k;
+  unsigned a_off[A_CHUNKS];
+  unsigned w_off[W_CHUNKS];
 #pragma unroll
-  for (int j = 0; j < A_LOADS; ++j) {
-    int64_t row = m0 + (t >> 3) + 32 * j;
-    row = row < m_rows ? row : m_rows - 1;
-    a_src[j] = aq + row * k + chunk * 16;
+  for (int q = 0; q < A_CHUNKS; ++q) {
+    const int r = 8 * (wave + WAVES * q) + cr;  // tile row
+    const int64_t row = m0 + r < m_rows ? r : m_rows - 1 - m0;
+    a_off[q] = static_cast<unsigned>(row * k + 16 * ((lane & 7) ^ (r & 7)));
   }
 #pragma unroll
-  for (int j = 0; j < W_LOADS; ++j) {
-    int64_t row = n0 + (t >> 3) + 32 * j;
-    row = row < n ? row : n - 1;
-    w_src[j] = wq + row * k + chunk * 16;
+  for (int q = 0; q < W_CHUNKS; ++q) {
+    const int r = 8 * (wave + WAVES * q) + cr;
+    const int64_t row = n0 + r < n ? r : n - 1 - n0;
+    w_off[q] = static_cast<unsigned>(row * k + 16 * ((lane & 7) ^ (r & 7)));
   }
-  const float* sw_row = ws + ((n0 < n ? n0 : n - 1) >> 7) * groups;
-  // Activation scale rows of this lane's tokens (one per 16-token sub-tile).
-  const float* sa_row[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    int64_t m = m0 + wave_m * WM + 16 * i + lrow;
-    m = m < m_rows ? m : m_rows - 1;
-    sa_row[i] = as + m * groups;
-  }
+  // Activation scales of the tile's tokens: wave w loads tokens
+  // 64 (w % (BM / 64)) .. + 63 (one dword each) into its own slot.
+  const float* sa_base = as + m0 * groups;
+  const int sa_t = 64 * (wave % (BM / 64)) + lane;
+  const int64_t sa_r = m0 + sa_t < m_rows ? sa_t : m_rows - 1 - m0;
+  const unsigned sa_off = static_cast<unsigned>(sa_r * groups);
+  int64_t wblock = n0 + TN * wave_n;
+  wblock = wblock < n ? wblock : n - 1;
+  const float* sw_src = ws + (wblock >> 7) * groups;
 
-  v4u a_stage[A_LOADS];
-  v4u w_stage[W_LOADS];
-  auto fetch = [&](int64_t g) {
-#pragma unroll
-    for (int j = 0; j < A_LOADS; ++j) a_stage[j] = *reinterpret_cast<const v4u*>(a_src[j] + g * kGroup);
-#pragma unroll
-    for (int j = 0; j < W_LOADS; ++j) w_stage[j] = *reinterpret_cast<const v4u*>(w_src[j] + g * kGroup);
-  };
-  auto park = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < A_LOADS; ++j)
-      *reinterpret_cast<v4u*>(&lds_a[buf][((t >> 3) + 32 * j) * kTileLdsStride + chunk * 16]) = a_stage[j];
-#pragma unroll
-    for (int j = 0; j < W_LOADS; ++j)
-      *reinterpret_cast<v4u*>(&lds_w[buf][((t >> 3) + 32 * j) * kTileLdsStride + chunk * 16]) = w_stage[j];
+  auto stage_base = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return lds0;
+    else if constexpr (decltype(st)::value == 1) return lds1;
+    else return lds2;
   };
 
-  v4f acc[TN][TM];
+  auto issue = [&](int64_t g, auto st) {
+    unsigned char* base = stage_base(st);
+    const unsigned char* ag = a_base + g * kGroup;
+    const unsigned char* wg = w_base + g * kGroup;
 #pragma unroll
-  for (int i = 0; i < TN; ++i)
+    for (int q = 0; q < A_CHUNKS; ++q) dma16(ag + a_off[q], base + 1024 * (wave + WAVES * q));
 #pragma unroll
-    for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < W_CHUNKS; ++q) dma16(wg + w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
+    dma4(sa_base + g + sa_off, base + (BM + BN) * 128 + 256 * wave);
+  };
 
-  fetch(0);
-  park(0);
-  __syncthreads();
+  // Fragment read: lane's row `r` of a 128-byte-row tile, chunks quarter and
+  // quarter + 4 (un-swizzled through c ^ (r & 7)).
+  auto frag = [&](const unsigned char* base, int r) -> v8i {
+    const int x = r & 7;
+    const v4u lo = *reinterpret_cast<const v4u*>(base + r * 128 + 16 * (quarter ^ x));
+    const v4u hi = *reinterpret_cast<const v4u*>(base + r * 128 + 16 * ((quarter + 4) ^ x));
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
 
-  for (int64_t g = 0; g < groups; ++g) {
-    const int buf = static_cast<int>(g & 1);
-    if (g + 1 < groups) fetch(g + 1);
+  v4f acc[I][J];
+#pragma unroll
+  for (int i = 0; i < I; ++i)
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // Operand reads: lane l takes row l % 16 of a sub-tile, bytes
-    // 16 (l / 16) .. +15 and 64 + 16 (l / 16) .. +15.
-    v8i wop[TN];
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const unsigned char* p = &lds_w[buf][(wave_n * WN + 16 * i + lrow) * kTileLdsStride + quarter * 16];
-      const v4u lo = *reinterpret_cast<const v4u*>(p);
-      const v4u hi = *reinterpret_cast<const v4u*>(p + 64);
-      wop[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-    v8i aop[TM];
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const unsigned char* p = &lds_a[buf][(wave_m * WM + 16 * j + lrow) * kTileLdsStride + quarter * 16];
-      const v4u lo = *reinterpret_cast<const v4u*>(p);
-      const v4u hi = *reinterpret_cast<const v4u*>(p + 64);
-      aop[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
-    const float sw = sw_row[g];
-    float sc[TM];
-#pragma unroll
-    for (int j = 0; j < TM; ++j) sc[j] = sa_row[j][g] * sw;
+  // Pipeline: step g computes from stage g % STAGES while the copies of the
+  // next STAGES - 1 steps are in flight. Copies are issued unconditionally
+  // (steps past the end re-copy the last step into a stage that is never
+  // read again), so every step has the same constant wait: step g + 1 must
+  // have landed, the STAGES - 2 later ones may not.
+  constexpr int kInFlight = (STAGES - 2) * KC::kLoadsPerWave;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  issue(0, S0{});
+  if constexpr (STAGES == 3) issue(groups > 1 ? 1 : 0, S1{});
+  wait_vm_barrier<kInFlight>();
 
+  auto step = [&](int64_t g, auto st) {
+    constexpr int cur = decltype(st)::value;
+    constexpr int nxt = (cur + STAGES - 1) % STAGES;  // stage of step g + STAGES - 1
+    const int64_t gn = g + STAGES - 1;
+    issue(gn < groups ? gn : groups - 1, std::integral_constant<int, nxt>{});
+
+    const unsigned char* la = stage_base(st);
+    const unsigned char* lw = la + BM * 128;
+    const float* ls = reinterpret_cast<const float*>(la + (BM + BN) * 128);
+    const float sw = sw_src[g];
+
+    v8i wf[I];
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
+    for (int i = 0; i < I; ++i) wf[i] = frag(lw, TN * wave_n + 16 * i + lrow);
+
+    // Token sub-tile j's MFMAs are issued before sub-tile j - 1's scale FMAs,
+    // so no FMA waits on the MFMA just issued.
+    v4f p_prev[I];
+    float sc_prev = 0.f;
+    v8i af = frag(la, TM * wave_m + lrow);
+    float sc = ls[TM * wave_m + lrow] * sw;
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const v4f p = mfma_16x16x128_e4m3(wop[i], aop[j]);
-        acc[i][j][0] = fmaf(sc[j], p[0], acc[i][j][0]);
-        acc[i][j][1] = fmaf(sc[j], p[1], acc[i][j][1]);
-        acc[i][j][2] = fmaf(sc[j], p[2], acc[i][j][2]);
-        acc[i][j][3] = fmaf(sc[j], p[3], acc[i][j][3]);
+    for (int j = 0; j < J; ++j) {
+      v8i af_next = af;
+      float sc_next = sc;
+      if (j + 1 < J) {
+        const int tr = TM * wave_m + 16 * (j + 1) + lrow;
+        af_next = frag(la, tr);
+        sc_next = ls[tr] * sw;
       }
-    }
-    if (g + 1 < groups) park(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: lane holds, for each sub-tile, rows n = 4 (l / 16) + 0..3 of
-  // token m = l % 16: four consecutive outputs of C's row m.
+      // MFMA (i, j), then the scale FMAs of (i, j - 1), whose MFMA was issued
+      // I MFMAs earlier: at most I + 1 fresh results are live.
+      v4f p_cur[I];
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    const int64_t m = m0 + wave_m * WM + 16 * j + lrow;
+      for (int i = 0; i < I; ++i) {
+        p_cur[i] = mfma_16x16x128_e4m3(wf[i], af);
+        if (j > 0) {
+          acc[i][j - 1][0] = fmaf(sc_prev, p_prev[i][0], acc[i][j - 1][0]);
+          acc[i][j - 1][1] = fmaf(sc_prev, p_prev[i][1], acc[i][j - 1][1]);
+          acc[i][j - 1][2] = fmaf(sc_prev, p_prev[i][2], acc[i][j - 1][2]);
+          acc[i][j - 1][3] = fmaf(sc_prev, p_prev[i][3], acc[i][j - 1][3]);
+        }
+        // Keep this order: left alone, the compiler issues all MFMAs of the
+        // step first and all FMAs afterwards, so that the matrix core and
+        // the VALU never overlap.
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < I; ++i) p_prev[i] = p_cur[i];
+      sc_prev = sc;
+      af = af_next;
+      sc = sc_next;
+    }
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      acc[i][J - 1][0] = fmaf(sc_prev, p_prev[i][0], acc[i][J - 1][0]);
+      acc[i][J - 1][1] = fmaf(sc_prev, p_prev[i][1], acc[i][J - 1][1]);
+      acc[i][J - 1][2] = fmaf(sc_prev, p_prev[i][2], acc[i][J - 1][2]);
+      acc[i][J - 1][3] = fmaf(sc_prev, p_prev[i][3], acc[i][J - 1][3]);
+    }
+
+    // Step g + 1's copies must have landed, and every wave must be done
+    // reading this stage before the next step's copies overwrite it.
+    wait_vm_barrier<kInFlight>();
+  };
+
+  for (int64_t g = 0; g < groups; g += STAGES) {
+    step(g, S0{});
+    if (g + 1 < groups) step(g + 1, S1{});
+    if constexpr (STAGES == 3) {
+      if (g + 2 < groups) step(g + 2, S2{});
+    }
+  }
+  // The copies issued past the last step must land before this workgroup's
+  // LDS can be handed to another one.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue: lane holds, per sub-tile, weight rows 4 (l / 16) .. +3 of token
+  // l % 16: four consecutive outputs in C's row.
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t m = m0 + TM * wave_m + 16 * j + lrow;
     if (m >= m_rows) continue;
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int64_t col = n0 + wave_n * WN + 16 * i + 4 * quarter;
+    for (int i = 0; i < I; ++i) {
+      const int64_t col = n0 + TN * wave_n + 16 * i + 4 * quarter;
       unsigned short* dst = c + m * n + col;
       const v4f v = acc[i][j];
       if ((n & 3) == 0 && col + 3 < n) {
