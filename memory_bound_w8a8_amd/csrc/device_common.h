@@ -52,6 +52,33 @@ __device__ __forceinline__ unsigned encode4_e4m3(float x0, float x1, float x2, f
   return static_cast<unsigned>(w);
 }
 
+// Raw buffer resource over [base, base + bytes) (bytes < 2^32). A buffer
+// load whose per-lane byte offset (the VGPR part plus the instruction's
+// immediate) is at or past `bytes` returns zeros without touching memory,
+// which the kernels use to mask absent rows and tokens. The uniform SGPR
+// offset of a load is kept in range by the caller and not relied on for that
+// check. Word 3 is the gfx9-family raw-buffer format (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// 16-byte and 4-byte buffer loads; the non-temporal form marks streamed data
+// that is read once.
+__device__ __forceinline__ v4u buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 0);
+}
+__device__ __forceinline__ v4u buffer_load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff), 2);
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+
+__device__ __forceinline__ v8i join8(const v4u& lo, const v4u& hi) {
+  return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 

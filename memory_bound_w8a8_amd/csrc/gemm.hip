@@ -5,8 +5,10 @@
 //   workgroup per CU; at most 16 * kMaxTiles rows, beyond that more
 //   workgroups), TILES = ceil(R / 16), and with S = 8 waves splitting the
 //   K / 128 groups, GMAX = ceil(groups / 8).
-// M only selects the token tile (16 or 32 tokens per MFMA column block), so
-// every M inside a tile runs the same instruction stream. Each (TILES, GMAX)
+// M only selects the token tile (16, 32 or 64 tokens: gemm_rows.h holds the
+// activation operand of all its groups in registers for up to 32 tokens,
+// gemm_rows64.h walks its groups in order for 33..64), so every M inside a
+// tile runs the same instruction stream. Each (TILES, GMAX)
 // pair has its own compiled instance, looked up exactly; shapes outside the
 // table (very large K) run the generic streaming kernel, which handles any
 // size with runtime loops.
@@ -15,6 +17,7 @@
 
 #include "device_common.h"
 #include "gemm_rows.h"
+#include "gemm_rows64.h"
 #include "gemm_stream.h"
 #include "gemm_tiled.h"
 #include "launch.h"
@@ -58,13 +61,34 @@ constexpr std::array<Launch, sizeof...(G)> rows_row(std::integer_sequence<int, G
   return {&rows_instance<MT, TILES, G + 1>...};
 }
 
+template <int TILES, int GMAX>
+hipError_t rows64_instance(const GemmArgs& a, int64_t rows_per_wg) {
+  // with one row tile the activation fragments in flight dominate the
+  // register budget: keep fewer weight chunks ahead
+  constexpr int PD = TILES == 1 ? 2 : 3;
+  const unsigned grid = static_cast<unsigned>((a.n + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((gemm_rows64_kernel<GMAX, TILES, PD>), dim3(grid), dim3(64 * kRowsWaves), 0, a.stream,
+                     static_cast<int>(a.m), a.n, a.k, rows_per_wg, static_cast<const unsigned char*>(a.aq), a.as,
+                     static_cast<const unsigned char*>(a.wq), a.ws, static_cast<unsigned short*>(a.c));
+  return hipGetLastError();
+}
+
+template <int MT, int TILES, int... G>
+constexpr std::array<Launch, sizeof...(G)> rows64_row(std::integer_sequence<int, G...>) {
+  return {&rows64_instance<TILES, G + 1>...};
+}
+
 template <int MT, int... T>
 constexpr std::array<std::array<Launch, kMaxGroupsPerWave>, sizeof...(T)> rows_table(std::integer_sequence<int, T...>) {
-  return {rows_row<MT, T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
+  if constexpr (MT == 64)
+    return {rows64_row<MT, T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
+  else
+    return {rows_row<MT, T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
 }
 
 constexpr auto kRows16 = rows_table<16>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows32 = rows_table<32>(std::make_integer_sequence<int, kMaxTiles>{});
+constexpr auto kRows64 = rows_table<64>(std::make_integer_sequence<int, kMaxTiles>{});
 
 template <int MT, int R, int S, int U>
 hipError_t stream_instance(const GemmArgs& a) {
@@ -91,7 +115,7 @@ bool rows_shape(int64_t m, int64_t n, int64_t k, int64_t* rows_per_wg, int* tile
   r = (r + 3) / 4 * 4;
   // A 32-token tile holding 7+ groups of activation operand leaves registers
   // for at most two row tiles' bookkeeping: use more, smaller workgroups.
-  const int64_t max_rows = (m > 16 && g >= 7) ? 32 : 16 * kMaxTiles;
+  const int64_t max_rows = (m > 16 && m <= 32 && g >= 7) ? 32 : 16 * kMaxTiles;
   if (r > max_rows) r = max_rows;
   *rows_per_wg = r;
   *tiles = static_cast<int>((r + 15) / 16);
@@ -104,8 +128,8 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
   const GemmArgs a{m, n, k, aq, as, wq, ws, c, stream};
   int64_t rows_per_wg;
   int tiles, gmax;
-  if (m <= 32 && rows_shape(m, n, k, &rows_per_wg, &tiles, &gmax)) {
-    const auto& table = m <= 16 ? kRows16 : kRows32;
+  if (rows_shape(m, n, k, &rows_per_wg, &tiles, &gmax)) {
+    const auto& table = m <= 16 ? kRows16 : (m <= 32 ? kRows32 : kRows64);
     return table[tiles - 1][gmax - 1](a, rows_per_wg);
   }
   // Generic streaming kernel: any N and K, 16-row slabs, runtime K loop.

@@ -67,7 +67,7 @@ TABLE_SHAPES = [(1000, 9216), (12800, 1024), (20000, 2304), (4100, 5120), (5000,
 
 
 @pytest.mark.parametrize("n,k", TABLE_SHAPES)
-@pytest.mark.parametrize("m", [1, 3, 8, 16, 17, 32])
+@pytest.mark.parametrize("m", [1, 3, 8, 16, 17, 32, 33, 64])
 def test_streaming_instance_table(m, n, k):
     a = workloads.activation(m, n, k)
     a_q, a_s = quant_act_ref(a)
