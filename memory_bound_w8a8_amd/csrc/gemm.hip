@@ -5,10 +5,8 @@
 //   workgroup per CU; at most 16 * kMaxTiles rows, beyond that more
 //   workgroups), TILES = ceil(R / 16), and with S = 8 waves splitting the
 //   K / 128 groups, GMAX = ceil(groups / 8).
-// M only selects the token tile (16, 32 or 64 tokens: gemm_rows.h holds the
-// activation operand of all its groups in registers for up to 32 tokens,
-// gemm_rows64.h walks its groups in order for 33..64), so every M inside a
-// tile runs the same instruction stream. Each (TILES, GMAX)
+// M only selects a token class (1..8, 9..16, 17..32, 33..64; see
+// rows_entry), so every M inside a class runs the same instruction stream. Each (TILES, GMAX)
 // pair has its own compiled instance, looked up exactly; shapes outside the
 // table (very large K) run the generic streaming kernel, which handles any
 // size with runtime loops.
@@ -43,22 +41,17 @@ struct GemmArgs {
 
 using Launch = hipError_t (*)(const GemmArgs&, int64_t rows_per_wg);
 
-template <int MT, int TILES, int GMAX>
+template <int MT, bool LINES, int TILES, int GMAX>
 hipError_t rows_instance(const GemmArgs& a, int64_t rows_per_wg) {
   // chunks of weight loads kept in flight per wave (fewer where the held
   // activation operand of a 32-token tile already takes most registers)
-  constexpr int PD = MT == 16 ? 6 : (GMAX <= 6 ? 4 : 2);
+  constexpr int PD = MT == 16 ? 6 : 4;
   const unsigned grid = static_cast<unsigned>((a.n + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((gemm_rows_kernel<MT, kRowsWaves, GMAX, TILES, PD>), dim3(grid), dim3(64 * kRowsWaves), 0,
+  hipLaunchKernelGGL((gemm_rows_kernel<MT, kRowsWaves, GMAX, TILES, PD, LINES>), dim3(grid), dim3(64 * kRowsWaves), 0,
                      a.stream, static_cast<int>(a.m), a.n, a.k, rows_per_wg,
                      static_cast<const unsigned char*>(a.aq), a.as, static_cast<const unsigned char*>(a.wq), a.ws,
                      static_cast<unsigned short*>(a.c));
   return hipGetLastError();
-}
-
-template <int MT, int TILES, int... G>
-constexpr std::array<Launch, sizeof...(G)> rows_row(std::integer_sequence<int, G...>) {
-  return {&rows_instance<MT, TILES, G + 1>...};
 }
 
 template <int TILES, int GMAX>
@@ -73,19 +66,32 @@ hipError_t rows64_instance(const GemmArgs& a, int64_t rows_per_wg) {
   return hipGetLastError();
 }
 
-template <int MT, int TILES, int... G>
-constexpr std::array<Launch, sizeof...(G)> rows64_row(std::integer_sequence<int, G...>) {
-  return {&rows64_instance<TILES, G + 1>...};
-}
-
-template <int MT, int... T>
-constexpr std::array<std::array<Launch, kMaxGroupsPerWave>, sizeof...(T)> rows_table(std::integer_sequence<int, T...>) {
-  if constexpr (MT == 64)
-    return {rows64_row<MT, T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
+// Token classes: up to 8 tokens (16-token tile, operand loaded directly),
+// 9..16 and 17..32 (16- and 32-token tiles, activation read as whole lines
+// and transposed), both holding the activation of all a wave's groups in
+// registers, which for 32 tokens fits up to 6 groups; 32 tokens with more
+// groups, and 33..64 tokens, run the group-major kernel.
+template <int TT, int TILES, int GMAX>
+constexpr Launch rows_entry() {
+  if constexpr (TT == 64 || (TT == 32 && GMAX > 6))
+    return &rows64_instance<TILES, GMAX>;
+  else if constexpr (TT == 8)
+    return &rows_instance<16, false, TILES, GMAX>;
   else
-    return {rows_row<MT, T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
+    return &rows_instance<TT, true, TILES, GMAX>;
 }
 
+template <int TT, int TILES, int... G>
+constexpr std::array<Launch, sizeof...(G)> rows_row(std::integer_sequence<int, G...>) {
+  return {rows_entry<TT, TILES, G + 1>()...};
+}
+
+template <int TT, int... T>
+constexpr std::array<std::array<Launch, kMaxGroupsPerWave>, sizeof...(T)> rows_table(std::integer_sequence<int, T...>) {
+  return {rows_row<TT, T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
+}
+
+constexpr auto kRows8 = rows_table<8>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows16 = rows_table<16>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows32 = rows_table<32>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows64 = rows_table<64>(std::make_integer_sequence<int, kMaxTiles>{});
@@ -105,17 +111,15 @@ __global__ void fill_zero_kernel(unsigned short* __restrict__ c, int64_t count) 
 
 }  // namespace
 
-// Row-range launch shape for (M, N, K): rows per workgroup, tiles, groups
+// Row-range launch shape for (N, K): rows per workgroup, tiles, groups
 // per wave. Returns false when the shape is outside the compiled table.
-bool rows_shape(int64_t m, int64_t n, int64_t k, int64_t* rows_per_wg, int* tiles, int* gmax) {
+bool rows_shape(int64_t n, int64_t k, int64_t* rows_per_wg, int* tiles, int* gmax) {
   const int64_t groups = k / kGroup;
   const int64_t g = (groups + kRowsWaves - 1) / kRowsWaves;
   if (g < 1 || g > kMaxGroupsPerWave) return false;
   int64_t r = (n + kNumCUs - 1) / kNumCUs;
   r = (r + 3) / 4 * 4;
-  // A 32-token tile holding 7+ groups of activation operand leaves registers
-  // for at most two row tiles' bookkeeping: use more, smaller workgroups.
-  const int64_t max_rows = (m > 16 && m <= 32 && g >= 7) ? 32 : 16 * kMaxTiles;
+  const int64_t max_rows = 16 * kMaxTiles;
   if (r > max_rows) r = max_rows;
   *rows_per_wg = r;
   *tiles = static_cast<int>((r + 15) / 16);
@@ -128,8 +132,8 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
   const GemmArgs a{m, n, k, aq, as, wq, ws, c, stream};
   int64_t rows_per_wg;
   int tiles, gmax;
-  if (rows_shape(m, n, k, &rows_per_wg, &tiles, &gmax)) {
-    const auto& table = m <= 16 ? kRows16 : (m <= 32 ? kRows32 : kRows64);
+  if (rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) {
+    const auto& table = m <= 8 ? kRows8 : m <= 16 ? kRows16 : m <= 32 ? kRows32 : kRows64;
     return table[tiles - 1][gmax - 1](a, rows_per_wg);
   }
   // Generic streaming kernel: any N and K, 16-row slabs, runtime K loop.

@@ -47,7 +47,7 @@
 
 namespace fp8bq {
 
-template <int MT, int S, int GMAX, int TILES, int PD>
+template <int MT, int S, int GMAX, int TILES, int PD, bool LINES>
 struct RowsKernel {
   static constexpr int kMS = MT / 16;        // 16-token tiles
   static constexpr int kChunks = TILES * GMAX;
@@ -56,14 +56,14 @@ struct RowsKernel {
   static constexpr int kLdsBytes = S * kStageSlots * 2048 + S * TILES * kMS * 1024;
 };
 
-template <int MT, int S, int GMAX, int TILES, int PD>
+template <int MT, int S, int GMAX, int TILES, int PD, bool LINES>
 __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n, int64_t k, int64_t rows_per_wg,
                                                            const unsigned char* __restrict__ aq,
                                                            const float* __restrict__ as,
                                                            const unsigned char* __restrict__ wq,
                                                            const float* __restrict__ ws,
                                                            unsigned short* __restrict__ c) {
-  using KC = RowsKernel<MT, S, GMAX, TILES, PD>;
+  using KC = RowsKernel<MT, S, GMAX, TILES, PD, LINES>;
   constexpr int MS = KC::kMS;
   constexpr int CH = KC::kChunks;
   constexpr int RING = KC::kRing;
@@ -88,32 +88,56 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
   __shared__ v4u stage[S][KC::kStageSlots][128];
   __shared__ v4f red[S][TILES][MS][64];
 
-  // Activation operand and scales of this wave's groups, same for all tiles.
+  // Per-lane load bases: rows 8 j + lane / 8 of each 16-row tile, piece
+  // lane % 8 (weights and activation alike: whole lines per instruction).
+  const int lr8 = lane >> 3;
+  const int piece = lane & 7;
+
+  // Activation operand and scales of this wave's groups, same for all
+  // tiles. Two load forms, chosen per instance:
+  //  - LINES: whole lines (tokens 16 s + 8 j + lane / 8, clamped), each
+  //    group transposed into the MFMA operand at its first use, in the first
+  //    row tile, while weight chunks are in flight. With many distinct tokens
+  //    this matters: every workgroup reads the same activation lines at about
+  //    the same time, and half-line requests from 16 token rows queue in a
+  //    few L2 channels.
+  //  - otherwise: the operand directly (token 16 s + lane % 16, pieces
+  //    quarter and quarter + 4). With few tokens the clamped rows coincide,
+  //    an instruction touches few lines, and no transposes are needed.
   v8i bv[GMAX][MS];
   float sa[GMAX][MS];
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
+    const unsigned char* ap0;
+    const unsigned char* ap1;
+    if constexpr (LINES) {
+      int m0 = 16 * s + lr8;
+      int m1 = m0 + 8;
+      m0 = m0 < m_rows ? m0 : m_rows - 1;
+      m1 = m1 < m_rows ? m1 : m_rows - 1;
+      ap0 = aq + static_cast<int64_t>(m0) * k + piece * 16;
+      ap1 = aq + static_cast<int64_t>(m1) * k + piece * 16;
+    } else {
+      int m0 = 16 * s + lrow;
+      m0 = m0 < m_rows ? m0 : m_rows - 1;
+      ap0 = aq + static_cast<int64_t>(m0) * k + quarter * 16;
+      ap1 = ap0 + 64;
+    }
     const int m = 16 * s + lrow;
     const bool mval = m < m_rows;
-    const int mc = mval ? m : m_rows - 1;
-    const unsigned char* ap = aq + static_cast<int64_t>(mc) * k + quarter * 16;
-    const float* sap = as + static_cast<int64_t>(mc) * groups;
+    const float* sap = as + static_cast<int64_t>(mval ? m : m_rows - 1) * groups;
 #pragma unroll
     for (int u = 0; u < GMAX; ++u) {
       const bool live = u < gcnt;
       const int g = live ? gbeg + u : glast;
       const int64_t off = static_cast<int64_t>(g) * kGroup;
-      const v4u lo = *reinterpret_cast<const v4u*>(ap + off);
-      const v4u hi = *reinterpret_cast<const v4u*>(ap + off + 64);
+      const v4u lo = *reinterpret_cast<const v4u*>(ap0 + off);
+      const v4u hi = *reinterpret_cast<const v4u*>(ap1 + off);
       bv[u][s] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
       const float scale = sap[g];
       sa[u][s] = (live && mval) ? scale : 0.f;
     }
   }
-
-  // Per-lane load bases: rows 8 j + lane / 8 of each tile, piece lane % 8.
-  const int lr8 = lane >> 3;
-  const int piece = lane & 7;
 
   v8i wv[RING];
   float sw[RING];
@@ -160,6 +184,10 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     if (u == 0) {
 #pragma unroll
       for (int s = 0; s < MS; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    if (LINES && t == 0) {  // first use of group u: its activation lines -> operand
+#pragma unroll
+      for (int s = 0; s < MS; ++s) bv[u][s] = transpose(bv[u][s], (ci + s + 1) & 1);
     }
     const v8i wop = transpose(wv[ci % RING], ci & 1);
 #pragma unroll
