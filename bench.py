@@ -12,8 +12,9 @@ weights rotate over enough distinct copies (>= 1 GiB) that no call finds its
 
 Printed: one JSON line with the step throughput (algorithmic bytes per step
 / step time, GB/s), per-M microseconds per call from HIP events on the
-launch stream, the roofline of the dominant kernel (the GEMM) and the CPU
-oracle timed on a bounded sample of the same workload.
+launch stream, the roofline of the dominant kernel (the GEMM), the prefill
+GEMMs (M = 3465) against the FP8 MFMA peak, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 
 import argparse
@@ -146,6 +147,52 @@ def time_kernels(plan, reps):
     return out
 
 
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
+
+
+def prefill(plan, reps=20):
+    """Prefill GEMMs (M = 3465 tokens, page 2 section 4.2) on the two logged
+    shapes that take it, timed with HIP events on the launch stream around
+    `reps` back-to-back calls: the compute-bound (MFMA) regime of the same
+    entry point. Weights and activations are synthetic and resident."""
+    dev = plan.dev
+    m = workloads.PREFILL_M
+    out = []
+    g = torch.Generator(device=dev)
+    for n, k in workloads.PREFILL_SHAPES:
+        if (n, k) == (N, K):
+            wq, ws = plan.w[0]
+        else:
+            g.manual_seed(99)
+            w32 = torch.randn((n, k), generator=g, device=dev, dtype=torch.float32).mul_(0.02)
+            wq, ws = fp8bq.quant_weight(w32)
+            del w32
+        g.manual_seed(7)
+        a = torch.randn((m, k), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        aq, as_ = fp8bq.quant_act(a)
+        c = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+        def call():
+            st = plan.lib.fp8bq_gemm(m, n, k, aq.data_ptr(), as_.data_ptr(), wq.data_ptr(), ws.data_ptr(),
+                                     c.data_ptr(), plan.s)
+            if st:
+                raise fp8bq.Fp8bqError("fp8bq_gemm", st)
+
+        call()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(plan.stream)
+        for _ in range(reps):
+            call()
+        e1.record(plan.stream)
+        e1.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tflops = 2.0 * m * n * k / (us * 1e-6) / 1e12
+        out.append({"M": m, "N": n, "K": k, "us": round(us, 2), "TFLOPs": round(tflops, 1),
+                    "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)})
+    return out
+
+
 def cpu_baseline(budget_s=20.0, rows=4096):
     """The CPU oracle (numpy, fp64 GEMM) on a bounded sample: quantise the
     activation and compute the GEMM for M = 1..8 against the first `rows`
@@ -164,7 +211,7 @@ def cpu_baseline(budget_s=20.0, rows=4096):
         w_s = np.concatenate([s for _, s in blocks])
         acts = {m: workloads.activation(m, N, K) for m in MS}
         passes, t_total, bytes_total = 0, 0.0, 0
-        while t_total < budget_s and passes < 20:
+        while t_total < budget_s and passes < 100:
             t0 = time.perf_counter()
             for m in MS:
                 a_q, a_s = quant_act_ref(acts[m])
@@ -189,6 +236,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--kernel-reps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the M=3465 prefill GEMM timing")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a dispatch of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -279,12 +327,16 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "gemm_rows_kernel (the M=1..8 launches; HIP events around back-to-back launches)",
+            "kernel": "gemm_rows_kernel<16, 8, 5, 5, 6, false> (the M=1..8 launches; HIP events on the launch "
+                      "stream around back-to-back launches)",
         },
         "wall_s_timed": round(wall, 3),
         "kernel_source_digest": digest,
         "device": torch.cuda.get_device_name(0),
     }
+    if not args.no_prefill:
+        print("bench: timing the prefill GEMMs", file=sys.stderr, flush=True)
+        rec["prefill"] = prefill(plan)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline()

@@ -144,7 +144,8 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
 
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                              const void* wq, const float* ws, void* c, hipStream_t stream) {
-  constexpr int BM = 256, BN = 128, WM = 4, WN = 2, STAGES = 3;
+  // 128 tokens x 256 weight rows per workgroup, 2 x 4 waves of 64 x 64
+  constexpr int BM = 128, BN = 256, WM = 2, WN = 4, STAGES = 3;
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WM, WN, STAGES>), dim3(static_cast<unsigned>(tiles)), dim3(64 * WM * WN), 0,
                      stream, m, n, k, static_cast<const unsigned char*>(aq), as,

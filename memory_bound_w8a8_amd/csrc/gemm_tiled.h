@@ -11,8 +11,9 @@
 // registers. K is walked one 128-wide scale group per step:
 //   1. the step's A slice (BM x 128 codes), W slice (BN x 128 codes) and the
 //      BM activation scales are copied global -> LDS with direct-to-LDS loads
-//      (no registers), double-buffered: step g + 1 is in flight while step g
-//      computes;
+//      (no registers), three stages deep: steps g + 1 and g + 2 are in
+//      flight while step g computes. The scales of one group are a strided
+//      gather (one line per token), so only BM / 64 waves copy them;
 //   2. each wave reads its W fragments once per step and streams its token
 //      fragments; one 16x16x128 FP8 MFMA per 16 x 16 sub-tile gives the
 //      group's exact products into a fresh accumulator (weight rows first
@@ -66,12 +67,13 @@ struct TiledKernel {
   static constexpr int kTN = BN / WN;  // weight rows per wave
   static constexpr int kJ = kTM / 16;  // token sub-tiles per wave
   static constexpr int kI = kTN / 16;  // weight-row sub-tiles per wave
-  // A codes, W codes, then one 64-token slot of activation scales per wave
-  // (waves past BM / 64 load a duplicate that is never read)
-  static constexpr int kStageBytes = (BM + BN) * 128 + kWaves * 64 * 4;
+  // A codes, W codes, then the BM activation scales (waves 0 .. BM / 64 - 1
+  // copy 64 each; the other waves copy none)
+  static constexpr int kStageBytes = (BM + BN) * 128 + BM * 4;
   static constexpr int kLdsBytes = STAGES * kStageBytes;
-  // direct-to-LDS loads one wave issues per K step
-  static constexpr int kLoadsPerWave = BM / 8 / kWaves + BN / 8 / kWaves + 1;
+  // direct-to-LDS loads one wave issues per K step (plus one for the waves
+  // that copy scales)
+  static constexpr int kTileLoadsPerWave = BM / 8 / kWaves + BN / 8 / kWaves;
 };
 
 // Wait until at most N of this wave's vector-memory operations are
@@ -180,10 +182,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
     const int64_t row = n0 + r < n ? r : n - 1 - n0;
     w_off[q] = static_cast<unsigned>(row * k + 16 * ((lane & 7) ^ (r & 7)));
   }
-  // Activation scales of the tile's tokens: wave w loads tokens
-  // 64 (w % (BM / 64)) .. + 63 (one dword each) into its own slot.
+  // Activation scales of the tile's tokens: wave w < BM / 64 copies tokens
+  // 64 w .. 64 w + 63 (one dword each: a 64-line gather, so only as many
+  // waves as there are distinct slots issue one).
+  const bool copies_scales = wave < BM / 64;
   const float* sa_base = as + m0 * groups;
-  const int sa_t = 64 * (wave % (BM / 64)) + lane;
+  const int sa_t = 64 * (copies_scales ? wave : 0) + lane;
   const int64_t sa_r = m0 + sa_t < m_rows ? sa_t : m_rows - 1 - m0;
   const unsigned sa_off = static_cast<unsigned>(sa_r * groups);
   int64_t wblock = n0 + TN * wave_n;
@@ -204,7 +208,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
     for (int q = 0; q < A_CHUNKS; ++q) dma16(ag + a_off[q], base + 1024 * (wave + WAVES * q));
 #pragma unroll
     for (int q = 0; q < W_CHUNKS; ++q) dma16(wg + w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
-    dma4(sa_base + g + sa_off, base + (BM + BN) * 128 + 256 * wave);
+    if (copies_scales) dma4(sa_base + g + sa_off, base + (BM + BN) * 128 + 256 * wave);
   };
 
   // Fragment read: lane's row `r` of a 128-byte-row tile, chunks quarter and
@@ -227,13 +231,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   // (steps past the end re-copy the last step into a stage that is never
   // read again), so every step has the same constant wait: step g + 1 must
   // have landed, the STAGES - 2 later ones may not.
-  constexpr int kInFlight = (STAGES - 2) * KC::kLoadsPerWave;
+  // (a wave's own copies: the scale-copying waves issue one more per step)
+  constexpr int kInFlight = (STAGES - 2) * KC::kTileLoadsPerWave;
+  constexpr int kInFlightScales = (STAGES - 2) * (KC::kTileLoadsPerWave + 1);
+  auto wait_step = [&]() {
+    if (copies_scales) wait_vm_barrier<kInFlightScales>();
+    else wait_vm_barrier<kInFlight>();
+  };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   issue(0, S0{});
   if constexpr (STAGES == 3) issue(groups > 1 ? 1 : 0, S1{});
-  wait_vm_barrier<kInFlight>();
+  wait_step();
 
   auto step = [&](int64_t g, auto st) {
     constexpr int cur = decltype(st)::value;
@@ -298,7 +308,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
 
     // Step g + 1's copies must have landed, and every wave must be done
     // reading this stage before the next step's copies overwrite it.
-    wait_vm_barrier<kInFlight>();
+    wait_step();
   };
 
   for (int64_t g = 0; g < groups; g += STAGES) {
