@@ -26,6 +26,8 @@ Modules:
   weight quantisation, fp32 arithmetic exactly as numpy float32 (IEEE RN).
 * ``gemm``  -- the dequantised block-scaled product in fp64, whole or at
   sampled output positions.
+* ``w8a16`` -- the weight-only variant (bf16 activation x block-FP8 weight,
+  page 1's W8A16 backend), fp64, whole or sampled.
 
 Every function is pinned by ``-m "not gpu"`` tests against something other
 than itself (torch's float8_e4m3fn casts, exact rational brute force, closed
@@ -35,6 +37,7 @@ forms and invariants). No function here is "parity unpinned".
 from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode_rne, e4m3_values
 from .quant import quant_act_ref, quant_weight_ref
 from .gemm import gemm_ref, gemm_ref_at
+from .w8a16 import gemm_w8a16_ref, gemm_w8a16_ref_at
 
 __all__ = [
     "E4M3_MAX",
@@ -45,4 +48,6 @@ __all__ = [
     "quant_weight_ref",
     "gemm_ref",
     "gemm_ref_at",
+    "gemm_w8a16_ref",
+    "gemm_w8a16_ref_at",
 ]

@@ -95,3 +95,27 @@ def gemm_exact(a_q, a_s, w_q, w_s, rows=None, cols=None):
             tot += Fraction(float(a_s[i, gi])) * Fraction(float(w_s[j // 128, gi])) * int(sums[gi])
         out.append(tot / (1 << 18))
     return out
+
+
+def gemm_w8a16_exact(a, w_q, w_s, rows=None, cols=None):
+    """Exact C[m, n] as Fractions for a bf16 activation (given as floats) and
+    block-FP8 weights: Fraction activation values times the 512x-scaled
+    integer codes, per group, times the Fraction weight scale."""
+    lut = [e4m3_int512(c) if c not in (0x7F, 0xFF) else 0 for c in range(256)]
+    a = np.asarray(a, dtype=np.float64)
+    w_q = np.asarray(w_q)
+    m, k = a.shape
+    n = w_q.shape[0]
+    g = k // 128
+    if rows is None:
+        pairs = [(i, j) for i in range(m) for j in range(n)]
+    else:
+        pairs = list(zip(rows, cols))
+    out = []
+    for i, j in pairs:
+        tot = Fraction(0)
+        for gi in range(g):
+            s = sum(Fraction(float(a[i, kk])) * lut[int(w_q[j, kk])] for kk in range(gi * 128, gi * 128 + 128))
+            tot += Fraction(float(w_s[j // 128, gi])) * s
+        out.append(tot / 512)
+    return out
