@@ -55,6 +55,13 @@ def quant_bytes(m, k):
     return 2 * m * k + m * k + 4 * m * (k // 128)
 
 
+def w8a16_bytes(m, n, k):
+    """Algorithmic bytes of one weight-only call: W codes + W scales + bf16
+    activation + C (bf16)."""
+    g = k // 128
+    return n * k + 4 * ((n + 127) // 128) * g + 2 * m * k + 2 * m * n
+
+
 def kernel_source_digest():
     """Hash of the sources that define the dominant kernel (the row-range
     streaming GEMM and its launch configuration), to tie stored counter data
@@ -123,10 +130,22 @@ class Plan:
         if st:
             raise fp8bq.Fp8bqError("fp8bq_gemm", st)
 
+    def w8a16(self, m):
+        wq, ws = self.w[self.next_w]
+        self.next_w = (self.next_w + 1) % len(self.w)
+        st = self.lib.fp8bq_gemm_w8a16(m, N, K, self.a[m].data_ptr(), wq.data_ptr(), ws.data_ptr(),
+                                       self.c[m].data_ptr(), self.s)
+        if st:
+            raise fp8bq.Fp8bqError("fp8bq_gemm_w8a16", st)
+
     def step(self):
         for m in MS:
             self.quant(m)
             self.gemm(m)
+
+    def step_w8a16(self):
+        for m in MS:
+            self.w8a16(m)
 
 
 def time_kernels(plan, reps):
@@ -134,7 +153,7 @@ def time_kernels(plan, reps):
     stream around `reps` back-to-back launches (rotating weights)."""
     out = {}
     for m in MS:
-        for kind, fn in (("gemm", plan.gemm), ("quant", plan.quant)):
+        for kind, fn in (("gemm", plan.gemm), ("quant", plan.quant), ("w8a16", plan.w8a16)):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             fn(m)
@@ -284,6 +303,20 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
+    # the same workload through the weight-only entry point: one launch per M
+    for _ in range(args.warmup):
+        plan.step_w8a16()
+    torch.cuda.synchronize()
+    e2 = torch.cuda.Event(enable_timing=True)
+    e3 = torch.cuda.Event(enable_timing=True)
+    e2.record(plan.stream)
+    for _ in range(args.steps):
+        plan.step_w8a16()
+    e3.record(plan.stream)
+    torch.cuda.synchronize()
+    ms_w8a16 = e2.elapsed_time(e3) / args.steps
+    w8a16_step_bytes = sum(w8a16_bytes(m, N, K) for m in MS)
+
     kt = time_kernels(plan, args.kernel_reps)
     step_bytes = sum(gemm_bytes(m, N, K) + quant_bytes(m, K) for m in MS)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -293,7 +326,9 @@ def main():
         us = kt[("gemm", m)]
         gbs = gemm_bytes(m, N, K) / (us * 1e-6) / 1e9
         per_m.append({"M": m, "gemm_us": round(us, 3), "gemm_GBps": round(gbs, 1),
-                      "gemm_pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "quant_act_us": round(kt[("quant", m)], 3)})
+                      "gemm_pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "quant_act_us": round(kt[("quant", m)], 3),
+                      "w8a16_us": round(kt[("w8a16", m)], 3),
+                      "w8a16_GBps": round(w8a16_bytes(m, N, K) / (kt[("w8a16", m)] * 1e-6) / 1e9, 1)})
     g_bytes = sum(gemm_bytes(m, N, K) for m in MS)
     g_time = sum(kt[("gemm", m)] for m in MS) * 1e-6
     achieved = g_bytes / g_time / 1e9
@@ -329,6 +364,14 @@ def main():
             "traffic": traffic,
             "kernel": "gemm_rows_kernel<16, 8, 5, 5, 6, false> (the M=1..8 launches; HIP events on the launch "
                       "stream around back-to-back launches)",
+        },
+        "w8a16": {
+            "path": "fp8bq_gemm_w8a16 (bf16 activation x block-FP8 weight, no activation quantisation), "
+                    "one launch per M, same weights and activations",
+            "ms_per_step": round(ms_w8a16, 5),
+            "value": round(w8a16_step_bytes / (ms_w8a16 * 1e-3) / 1e9, 1),
+            "unit": "GB/s",
+            "step_bytes": w8a16_step_bytes,
         },
         "wall_s_timed": round(wall, 3),
         "kernel_source_digest": digest,

@@ -125,6 +125,29 @@ int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_f
                       const float *A_scales, const void *W_fp8, const float *W_scales,
                       void *C_bf16, void *stream);
 
+/*
+ * Weight-only block-FP8 GEMM (page 1, SmartX blog, "single-stream
+ * optimisation": the W8A16 backend keeps the activation in 16 bits and skips
+ * the per-call activation quantisation; it was the faster backend at one
+ * stream and the slower one at high concurrency, so this entry point serves
+ * small batches only).
+ *
+ *   C[m, n] = sum_g W_scales[n / 128, g]
+ *                   * sum_{k = 128g}^{128g+127} A[m, k] * dec(W_fp8[n, k])
+ *
+ *   A_bf16   [M, K] bf16, read; 1 <= M <= 16
+ *   W_fp8    [N, K] uint8 codes, W_scales [ceil(N/128), K/128] fp32 (read),
+ *            the same weights fp8bq_gemm takes
+ *   C_bf16   [M, N] bf16, written; products exact, fp32 accumulation,
+ *            rounded to bf16 RNE. Two identical calls give identical bits.
+ * M == 0 or N == 0 is a quick return; K == 0 writes zeros. Errors: NULL
+ * pointer; negative size; K % 128 != 0; M > 16; K > 9216 (more than 72
+ * groups); M*K, N*K or M*N > 2^40; A_bf16, W_fp8 or C_bf16 not 16-B aligned,
+ * W_scales not 4-B aligned; device not gfx950.
+ */
+int fp8bq_gemm_w8a16(int64_t M, int64_t N, int64_t K, const void *A_bf16, const void *W_fp8,
+                     const float *W_scales, void *C_bf16, void *stream);
+
 /* Human-readable name of a status code; never NULL. */
 const char *fp8bq_status_string(int status);
 

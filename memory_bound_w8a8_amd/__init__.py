@@ -29,6 +29,7 @@ EXPORTS = (
     "fp8bq_gemm",
     "fp8bq_gemm_path",
     "fp8bq_gemm_forced",
+    "fp8bq_gemm_w8a16",
     "fp8bq_status_string",
 )
 
@@ -57,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_gemm.argtypes = [i64, i64, i64, vp, fp, vp, fp, vp, vp]
         L.fp8bq_gemm_forced.argtypes = [ctypes.c_int, i64, i64, i64, vp, fp, vp, fp, vp, vp]
         L.fp8bq_gemm_path.argtypes = [i64, i64, i64]
+        L.fp8bq_gemm_w8a16.argtypes = [i64, i64, i64, vp, vp, fp, vp, vp]
         L.fp8bq_status_string.argtypes = [ctypes.c_int]
         L.fp8bq_status_string.restype = ctypes.c_char_p
         for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path"):
@@ -147,6 +149,31 @@ def gemm(a_q, a_s, w_q, w_s, out=None) -> torch.Tensor:
     with torch.cuda.device(a_q.device):
         st = lib().fp8bq_gemm(m, n, k, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(out), _stream(a_q))
     _check("fp8bq_gemm", st)
+    return out
+
+
+def gemm_w8a16(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
+    """Weight-only block-FP8 GEMM: bf16 activation [M, K] (M <= 16) times the
+    block-FP8 weight, bf16 [M, N]."""
+    w_q = _codes(w_q)
+    _need(a, "a", torch.bfloat16, 2)
+    _need(w_q, "w_q", torch.uint8, 2)
+    _need(w_s, "w_s", torch.float32, 2)
+    m, k = a.shape
+    n, k2 = w_q.shape
+    if k != k2:
+        raise ValueError(f"K mismatch: a has {k}, w_q has {k2}")
+    if tuple(w_s.shape) != ((n + 127) // 128, k // 128):
+        raise ValueError(f"weight scale shape {tuple(w_s.shape)} does not match N={n}, K={k}")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    else:
+        _need(out, "out", torch.bfloat16, 2)
+        if tuple(out.shape) != (m, n):
+            raise ValueError(f"out must be [{m}, {n}]")
+    with torch.cuda.device(a.device):
+        st = lib().fp8bq_gemm_w8a16(m, n, k, _ptr(a), _ptr(w_q), _ptr(w_s), _ptr(out), _stream(a))
+    _check("fp8bq_gemm_w8a16", st)
     return out
 
 

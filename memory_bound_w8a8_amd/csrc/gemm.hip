@@ -18,6 +18,7 @@
 #include "gemm_rows64.h"
 #include "gemm_stream.h"
 #include "gemm_tiled.h"
+#include "gemm_w8a16.h"
 #include "launch.h"
 
 namespace fp8bq {
@@ -91,6 +92,30 @@ constexpr std::array<std::array<Launch, kMaxGroupsPerWave>, sizeof...(T)> rows_t
   return {rows_row<TT, T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
 }
 
+// Weight-only (bf16 activation) instances, up to 16 tokens.
+template <int TILES, int GMAX>
+hipError_t w8a16_instance(const GemmArgs& a, int64_t rows_per_wg) {
+  // 16 activation registers per group: keep fewer chunks ahead at large K
+  constexpr int PD = GMAX >= 8 ? 2 : (GMAX >= 7 ? 4 : 6);
+  const unsigned grid = static_cast<unsigned>((a.n + rows_per_wg - 1) / rows_per_wg);
+  hipLaunchKernelGGL((gemm_w8a16_kernel<GMAX, TILES, PD>), dim3(grid), dim3(64 * kRowsWaves), 0, a.stream,
+                     static_cast<int>(a.m), a.n, a.k, rows_per_wg, static_cast<const unsigned short*>(a.aq),
+                     static_cast<const unsigned char*>(a.wq), a.ws, static_cast<unsigned short*>(a.c));
+  return hipGetLastError();
+}
+
+template <int TILES, int... G>
+constexpr std::array<Launch, sizeof...(G)> w8a16_row(std::integer_sequence<int, G...>) {
+  return {&w8a16_instance<TILES, G + 1>...};
+}
+
+template <int... T>
+constexpr std::array<std::array<Launch, kMaxGroupsPerWave>, sizeof...(T)> w8a16_table(std::integer_sequence<int, T...>) {
+  return {w8a16_row<T + 1>(std::make_integer_sequence<int, kMaxGroupsPerWave>{})...};
+}
+
+constexpr auto kW8A16 = w8a16_table(std::make_integer_sequence<int, kMaxTiles>{});
+
 constexpr auto kRows8 = rows_table<8>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows16 = rows_table<16>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows32 = rows_table<32>(std::make_integer_sequence<int, kMaxTiles>{});
@@ -140,6 +165,21 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
   if (m <= 16) return stream_instance<16, 1, 8, 5>(a);
   if (m <= 32) return stream_instance<32, 1, 8, 4>(a);
   return stream_instance<64, 1, 8, 2>(a);
+}
+
+bool w8a16_supported(int64_t m, int64_t n, int64_t k) {
+  int64_t rows_per_wg;
+  int tiles, gmax;
+  return m >= 1 && m <= 16 && rows_shape(n, k, &rows_per_wg, &tiles, &gmax);
+}
+
+hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, const void* wq, const float* ws, void* c,
+                             hipStream_t stream) {
+  const GemmArgs args{m, n, k, a, nullptr, wq, ws, c, stream};
+  int64_t rows_per_wg;
+  int tiles, gmax;
+  if (m < 1 || m > 16 || !rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) return hipErrorInvalidValue;
+  return kW8A16[tiles - 1][gmax - 1](args, rows_per_wg);
 }
 
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,

@@ -18,6 +18,12 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                              const void* wq, const float* ws, void* c, hipStream_t stream);
 
+// Weight-only (bf16 activation) streaming kernel, 1 <= m <= 16 and K/128
+// groups within the instance table (w8a16_supported).
+bool w8a16_supported(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, const void* wq, const float* ws, void* c,
+                             hipStream_t stream);
+
 // C = 0 (used for K == 0).
 hipError_t launch_fill_zero_bf16(int64_t count, void* c, hipStream_t stream);
 
