@@ -143,6 +143,18 @@ class Plan:
             self.quant(m)
             self.gemm(m)
 
+    def fused(self, m):
+        wq, ws = self.w[self.next_w]
+        self.next_w = (self.next_w + 1) % len(self.w)
+        st = self.lib.fp8bq_gemm_fused(m, N, K, self.a[m].data_ptr(), wq.data_ptr(), ws.data_ptr(),
+                                       self.c[m].data_ptr(), self.s)
+        if st:
+            raise fp8bq.Fp8bqError("fp8bq_gemm_fused", st)
+
+    def step_fused(self):
+        for m in MS:
+            self.fused(m)
+
     def step_w8a16(self):
         for m in MS:
             self.w8a16(m)
@@ -153,7 +165,7 @@ def time_kernels(plan, reps):
     stream around `reps` back-to-back launches (rotating weights)."""
     out = {}
     for m in MS:
-        for kind, fn in (("gemm", plan.gemm), ("quant", plan.quant), ("w8a16", plan.w8a16)):
+        for kind, fn in (("gemm", plan.gemm), ("quant", plan.quant), ("w8a16", plan.w8a16), ("fused", plan.fused)):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             fn(m)
@@ -303,18 +315,23 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # the same workload through the weight-only entry point: one launch per M
-    for _ in range(args.warmup):
-        plan.step_w8a16()
-    torch.cuda.synchronize()
-    e2 = torch.cuda.Event(enable_timing=True)
-    e3 = torch.cuda.Event(enable_timing=True)
-    e2.record(plan.stream)
-    for _ in range(args.steps):
-        plan.step_w8a16()
-    e3.record(plan.stream)
-    torch.cuda.synchronize()
-    ms_w8a16 = e2.elapsed_time(e3) / args.steps
+    def time_steps(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ea = torch.cuda.Event(enable_timing=True)
+        eb = torch.cuda.Event(enable_timing=True)
+        ea.record(plan.stream)
+        for _ in range(args.steps):
+            fn()
+        eb.record(plan.stream)
+        torch.cuda.synchronize()
+        return ea.elapsed_time(eb) / args.steps
+
+    # the same workload with quantisation fused into the GEMM, and through
+    # the weight-only entry point: one launch per M each
+    ms_fused = time_steps(plan.step_fused)
+    ms_w8a16 = time_steps(plan.step_w8a16)
     w8a16_step_bytes = sum(w8a16_bytes(m, N, K) for m in MS)
 
     kt = time_kernels(plan, args.kernel_reps)
@@ -327,6 +344,7 @@ def main():
         gbs = gemm_bytes(m, N, K) / (us * 1e-6) / 1e9
         per_m.append({"M": m, "gemm_us": round(us, 3), "gemm_GBps": round(gbs, 1),
                       "gemm_pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "quant_act_us": round(kt[("quant", m)], 3),
+                      "fused_us": round(kt[("fused", m)], 3),
                       "w8a16_us": round(kt[("w8a16", m)], 3),
                       "w8a16_GBps": round(w8a16_bytes(m, N, K) / (kt[("w8a16", m)] * 1e-6) / 1e9, 1)})
     g_bytes = sum(gemm_bytes(m, N, K) for m in MS)
@@ -364,6 +382,14 @@ def main():
             "traffic": traffic,
             "kernel": "gemm_rows_kernel<16, 8, 5, 5, 6, false> (the M=1..8 launches; HIP events on the launch "
                       "stream around back-to-back launches)",
+        },
+        "fused": {
+            "path": "fp8bq_gemm_fused (activation quantisation inside the block-FP8 GEMM, bitwise the two-call "
+                    "result), one launch per M, same weights and activations",
+            "ms_per_step": round(ms_fused, 5),
+            "value": round(w8a16_step_bytes / (ms_fused * 1e-3) / 1e9, 1),
+            "unit": "GB/s",
+            "step_bytes": w8a16_step_bytes,
         },
         "w8a16": {
             "path": "fp8bq_gemm_w8a16 (bf16 activation x block-FP8 weight, no activation quantisation), "

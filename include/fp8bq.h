@@ -126,6 +126,26 @@ int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_f
                       void *C_bf16, void *stream);
 
 /*
+ * Activation quantisation and block-FP8 GEMM in one launch (page 1, SmartX
+ * blog, "single-stream optimisation": the W8A8 backend's per-call
+ * activation quantisation is a separate launch at every linear layer; here
+ * it runs inside the GEMM).
+ *
+ *   C = fp8bq_gemm(fp8bq_quant_act(A_bf16), W_fp8, W_scales)
+ *
+ *   A_bf16   [M, K] bf16, read; 1 <= M <= 16
+ *   W_fp8, W_scales as fp8bq_gemm; C_bf16 [M, N] bf16, written.
+ * The codes and scales formed inside are exactly those fp8bq_quant_act
+ * writes, and C is bitwise the two-call result; they are not stored.
+ * M == 0 or N == 0 is a quick return; K == 0 writes zeros. Errors: NULL
+ * pointer; negative size; K % 128 != 0; M > 16; K > 9216 (more than 72
+ * groups); M*K, N*K or M*N > 2^40; A_bf16, W_fp8 or C_bf16 not 16-B aligned,
+ * W_scales not 4-B aligned; device not gfx950.
+ */
+int fp8bq_gemm_fused(int64_t M, int64_t N, int64_t K, const void *A_bf16, const void *W_fp8,
+                     const float *W_scales, void *C_bf16, void *stream);
+
+/*
  * Weight-only block-FP8 GEMM (page 1, SmartX blog, "single-stream
  * optimisation": the W8A16 backend keeps the activation in 16 bits and skips
  * the per-call activation quantisation; it was the faster backend at one

@@ -29,6 +29,7 @@ EXPORTS = (
     "fp8bq_gemm",
     "fp8bq_gemm_path",
     "fp8bq_gemm_forced",
+    "fp8bq_gemm_fused",
     "fp8bq_gemm_w8a16",
     "fp8bq_status_string",
 )
@@ -59,6 +60,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_gemm_forced.argtypes = [ctypes.c_int, i64, i64, i64, vp, fp, vp, fp, vp, vp]
         L.fp8bq_gemm_path.argtypes = [i64, i64, i64]
         L.fp8bq_gemm_w8a16.argtypes = [i64, i64, i64, vp, vp, fp, vp, vp]
+        L.fp8bq_gemm_fused.argtypes = [i64, i64, i64, vp, vp, fp, vp, vp]
         L.fp8bq_status_string.argtypes = [ctypes.c_int]
         L.fp8bq_status_string.restype = ctypes.c_char_p
         for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path"):
@@ -152,9 +154,7 @@ def gemm(a_q, a_s, w_q, w_s, out=None) -> torch.Tensor:
     return out
 
 
-def gemm_w8a16(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
-    """Weight-only block-FP8 GEMM: bf16 activation [M, K] (M <= 16) times the
-    block-FP8 weight, bf16 [M, N]."""
+def _bf16_act_args(a, w_q, w_s, out):
     w_q = _codes(w_q)
     _need(a, "a", torch.bfloat16, 2)
     _need(w_q, "w_q", torch.uint8, 2)
@@ -171,9 +171,26 @@ def gemm_w8a16(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
         _need(out, "out", torch.bfloat16, 2)
         if tuple(out.shape) != (m, n):
             raise ValueError(f"out must be [{m}, {n}]")
+    return w_q, m, n, k, out
+
+
+def gemm_w8a16(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
+    """Weight-only block-FP8 GEMM: bf16 activation [M, K] (M <= 16) times the
+    block-FP8 weight, bf16 [M, N]."""
+    w_q, m, n, k, out = _bf16_act_args(a, w_q, w_s, out)
     with torch.cuda.device(a.device):
         st = lib().fp8bq_gemm_w8a16(m, n, k, _ptr(a), _ptr(w_q), _ptr(w_s), _ptr(out), _stream(a))
     _check("fp8bq_gemm_w8a16", st)
+    return out
+
+
+def gemm_fused(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
+    """Activation quantisation and block-FP8 GEMM in one launch: bf16 [M, K]
+    (M <= 16) -> bf16 [M, N], bitwise gemm(*quant_act(a), w_q, w_s)."""
+    w_q, m, n, k, out = _bf16_act_args(a, w_q, w_s, out)
+    with torch.cuda.device(a.device):
+        st = lib().fp8bq_gemm_fused(m, n, k, _ptr(a), _ptr(w_q), _ptr(w_s), _ptr(out), _stream(a))
+    _check("fp8bq_gemm_fused", st)
     return out
 
 

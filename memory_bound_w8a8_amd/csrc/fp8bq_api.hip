@@ -14,8 +14,8 @@ constexpr int64_t kMaxElems = int64_t(1) << 40;  // bound on M*K, N*K, M*N
 constexpr int64_t kStreamMaxM = 64;              // streaming kernel serves 1..64
 constexpr int64_t kTiledMaxK = int64_t(1) << 24; // tiled kernel: 32-bit offsets within a 256-row tile
 constexpr int kMaxDevices = 64;
-constexpr int64_t kW8A16MaxM = 16;               // weight-only path: one 16-token tile
-constexpr int64_t kW8A16MaxK = 72 * 128;         // groups within its instance table
+constexpr int64_t kSmallMaxM = 16;               // fused and weight-only paths: one 16-token tile
+constexpr int64_t kSmallMaxK = 72 * 128;         // groups within their instance tables
 
 // Per-device capability cache: 0 = unknown, 1 = gfx950, -1 = not usable.
 std::atomic<int> g_device_ok[kMaxDevices];
@@ -117,11 +117,11 @@ int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K) {
   return gemm_path(M);
 }
 
-int fp8bq_gemm_w8a16(int64_t M, int64_t N, int64_t K, const void* A_bf16, const void* W_fp8, const float* W_scales,
+int fp8bq_gemm_fused(int64_t M, int64_t N, int64_t K, const void* A_bf16, const void* W_fp8, const float* W_scales,
                      void* C_bf16, void* stream) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
   if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
-  if (M > kW8A16MaxM || K > kW8A16MaxK) return FP8BQ_ERR_SHAPE;
+  if (M > kSmallMaxM || K > kSmallMaxK) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_OK;
   if (C_bf16 == nullptr) return FP8BQ_ERR_NULL;
   if (!aligned(C_bf16, 16)) return FP8BQ_ERR_ALIGN;
@@ -133,7 +133,27 @@ int fp8bq_gemm_w8a16(int64_t M, int64_t N, int64_t K, const void* A_bf16, const 
   if (st != FP8BQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) return launch_status(fp8bq::launch_fill_zero_bf16(M * N, C_bf16, s));
-  if (!fp8bq::w8a16_supported(M, N, K)) return FP8BQ_ERR_SHAPE;
+  if (!fp8bq::small_m_supported(M, N, K)) return FP8BQ_ERR_SHAPE;
+  return launch_status(fp8bq::launch_gemm_fused(M, N, K, A_bf16, W_fp8, W_scales, C_bf16, s));
+}
+
+int fp8bq_gemm_w8a16(int64_t M, int64_t N, int64_t K, const void* A_bf16, const void* W_fp8, const float* W_scales,
+                     void* C_bf16, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
+  if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
+  if (M > kSmallMaxM || K > kSmallMaxK) return FP8BQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BQ_OK;
+  if (C_bf16 == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(C_bf16, 16)) return FP8BQ_ERR_ALIGN;
+  if (K > 0) {
+    if (A_bf16 == nullptr || W_fp8 == nullptr || W_scales == nullptr) return FP8BQ_ERR_NULL;
+    if (!aligned(A_bf16, 16) || !aligned(W_fp8, 16) || !aligned(W_scales, 4)) return FP8BQ_ERR_ALIGN;
+  }
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return launch_status(fp8bq::launch_fill_zero_bf16(M * N, C_bf16, s));
+  if (!fp8bq::small_m_supported(M, N, K)) return FP8BQ_ERR_SHAPE;
   return launch_status(fp8bq::launch_gemm_w8a16(M, N, K, A_bf16, W_fp8, W_scales, C_bf16, s));
 }
 

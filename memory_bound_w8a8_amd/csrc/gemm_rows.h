@@ -47,7 +47,69 @@
 
 namespace fp8bq {
 
-template <int MT, int S, int GMAX, int TILES, int PD, bool LINES>
+// Activation forms the row-range kernel takes.
+enum ActForm : int {
+  kActCodes = 0,      // e4m3fn codes + scales, operand loaded directly
+  kActCodeLines = 1,  // e4m3fn codes + scales, whole lines + LDS transpose
+  kActBf16 = 2,       // bf16 activation, quantised in the kernel
+};
+
+// Quantise one group of a lane's token inside the MFMA operand layout: the
+// lane holds bf16 elements 16 q .. 16 q + 15 and 64 + 16 q .. 64 + 16 q + 15
+// of the group (q = lane / 16, four 16-byte pieces); lanes l, l ^ 16, l ^ 32,
+// l ^ 48 hold the rest of the same token's group. Same rule as
+// quant_act_kernel: amax over the 128 values, s = amax / 448 (IEEE; 1 for
+// an all-zero group), code = RNE(clamp(x / s, +-448)). Returns the 32 codes
+// in operand byte order and sets the scale.
+//
+// The quotient uses the correctly rounded reciprocal y = 1 / s once per
+// group and, per value, q0 = x y, r = fma(-q0, s, x) (exact), q = q0 if
+// r == 0 else fma(r, y, q0). An exhaustive GPU check over every bf16 x and
+// every bf16 amax >= |x| found the e4m3 codes of this quotient equal to
+// those of the IEEE division whenever amax >= 2^-104; below 2^-96 the IEEE
+// division is used instead.
+__device__ __forceinline__ v8i quant_group_operand(const v4u (&raw)[4], float* scale) {
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      x[8 * i + 2 * w] = bf16_lo(raw[i][w]);
+      x[8 * i + 2 * w + 1] = bf16_hi(raw[i][w]);
+    }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  const float s = group_scale(amax);
+  *scale = s;
+  v8i out;
+  if (amax >= 0x1p-96f) {
+    const float y = 1.0f / s;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      float q[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xv = x[4 * d + e];
+        const float q0 = xv * y;
+        const float r = fmaf(-q0, s, xv);
+        const float qq = r == 0.f ? q0 : fmaf(r, y, q0);
+        q[e] = fminf(fmaxf(qq, -kE4m3Max), kE4m3Max);
+      }
+      out[d] = static_cast<int>(encode4_e4m3(q[0], q[1], q[2], q[3]));
+    }
+  } else {
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      out[d] = static_cast<int>(encode4_e4m3(scaled_clamped(x[4 * d], s), scaled_clamped(x[4 * d + 1], s),
+                                             scaled_clamped(x[4 * d + 2], s), scaled_clamped(x[4 * d + 3], s)));
+  }
+  return out;
+}
+
+template <int MT, int S, int GMAX, int TILES, int PD, int AF>
 struct RowsKernel {
   static constexpr int kMS = MT / 16;        // 16-token tiles
   static constexpr int kChunks = TILES * GMAX;
@@ -56,14 +118,22 @@ struct RowsKernel {
   static constexpr int kLdsBytes = S * kStageSlots * 2048 + S * TILES * kMS * 1024;
 };
 
-template <int MT, int S, int GMAX, int TILES, int PD, bool LINES>
+template <int MT, int S, int GMAX, int TILES, int PD, int AF>
 __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n, int64_t k, int64_t rows_per_wg,
                                                            const unsigned char* __restrict__ aq,
                                                            const float* __restrict__ as,
                                                            const unsigned char* __restrict__ wq,
                                                            const float* __restrict__ ws,
                                                            unsigned short* __restrict__ c) {
-  using KC = RowsKernel<MT, S, GMAX, TILES, PD, LINES>;
+  using KC = RowsKernel<MT, S, GMAX, TILES, PD, AF>;
+  constexpr bool LINES = AF == kActCodeLines;
+  constexpr bool BF16 = AF == kActBf16;
+  static_assert(!BF16 || MT == 16, "in-kernel quantisation serves one 16-token tile");
+  // Chunk order. Tile-major (all groups of tile 0, then tile 1, ...) keeps
+  // one accumulator set; with in-kernel quantisation the order is
+  // group-major instead, so that each group's quantisation (at its first
+  // chunk) falls every TILES chunks rather than all within the first tile.
+  constexpr bool GROUP_MAJOR = BF16;
   constexpr int MS = KC::kMS;
   constexpr int CH = KC::kChunks;
   constexpr int RING = KC::kRing;
@@ -94,18 +164,30 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
   const int piece = lane & 7;
 
   // Activation operand and scales of this wave's groups, same for all
-  // tiles. Two load forms, chosen per instance:
-  //  - LINES: whole lines (tokens 16 s + 8 j + lane / 8, clamped), each
-  //    group transposed into the MFMA operand at its first use, in the first
-  //    row tile, while weight chunks are in flight. With many distinct tokens
-  //    this matters: every workgroup reads the same activation lines at about
-  //    the same time, and half-line requests from 16 token rows queue in a
-  //    few L2 channels.
-  //  - otherwise: the operand directly (token 16 s + lane % 16, pieces
+  // tiles. Load forms (AF):
+  //  - kActCodeLines: whole lines (tokens 16 s + 8 j + lane / 8, clamped),
+  //    each group transposed into the MFMA operand at its first use, in the
+  //    first row tile, while weight chunks are in flight. With many distinct
+  //    tokens this matters: every workgroup reads the same activation lines
+  //    at about the same time, and half-line requests from 16 token rows
+  //    queue in a few L2 channels.
+  //  - kActCodes: the operand directly (token 16 s + lane % 16, pieces
   //    quarter and quarter + 4). With few tokens the clamped rows coincide,
   //    an instruction touches few lines, and no transposes are needed.
+  //  - kActBf16: the bf16 values of those operand positions (`aq` then
+  //    points at bf16 data, `as` is unused), quantised into codes and a
+  //    scale at the group's first use (quant_group_operand).
   v8i bv[GMAX][MS];
   float sa[GMAX][MS];
+  // (kActBf16: loaded with the group's first weight chunk, PD chunks ahead
+  // of its first use, in load_chunk below; group-major order uses a group
+  // for TILES consecutive chunks, so only a few groups are ever live.)
+  v4u araw[BF16 ? GMAX : 1][4];
+  const unsigned short* arow = nullptr;
+  if constexpr (BF16) {
+    const int tok = lrow < m_rows ? lrow : m_rows - 1;
+    arow = reinterpret_cast<const unsigned short*>(aq) + static_cast<int64_t>(tok) * k + 16 * quarter;
+  } else {
 #pragma unroll
   for (int s = 0; s < MS; ++s) {
     const unsigned char* ap0;
@@ -138,14 +220,22 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
       sa[u][s] = (live && mval) ? scale : 0.f;
     }
   }
+  }
 
   v8i wv[RING];
   float sw[RING];
 
   auto load_chunk = [&](int ci, int slot) {
-    const int t = ci / GMAX;
-    const int u = ci - t * GMAX;
+    const int t = GROUP_MAJOR ? ci % TILES : ci / GMAX;
+    const int u = GROUP_MAJOR ? ci / TILES : ci % GMAX;
     const int g = u < gcnt ? gbeg + u : glast;
+    if (BF16 && t == 0) {
+      const unsigned short* p = arow + static_cast<int64_t>(g) * kGroup;
+      araw[u][0] = *reinterpret_cast<const v4u*>(p);
+      araw[u][1] = *reinterpret_cast<const v4u*>(p + 8);
+      araw[u][2] = *reinterpret_cast<const v4u*>(p + 64);
+      araw[u][3] = *reinterpret_cast<const v4u*>(p + 72);
+    }
     const int64_t off = static_cast<int64_t>(g) * kGroup + piece * 16;
     int64_t row0 = r_begin + 16 * t + lr8;
     int64_t row1 = row0 + 8;
@@ -173,17 +263,30 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
 
-  v4f acc[MS];
+  // Accumulators: one set per tile in group-major order, else one set
+  // reused tile after tile. Either way every output sums its groups in the
+  // same order 0, 1, ..., so the two orders give bitwise the same result.
+  v4f acc[GROUP_MAJOR ? TILES : 1][MS];
+#pragma unroll
+  for (int t = 0; t < (GROUP_MAJOR ? TILES : 1); ++t)
+#pragma unroll
+    for (int s = 0; s < MS; ++s) acc[t][s] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ci = 0; ci < PD && ci < CH; ++ci) load_chunk(ci, ci % RING);
 #pragma unroll
   for (int ci = 0; ci < CH; ++ci) {
-    const int t = ci / GMAX;
-    const int u = ci - t * GMAX;
+    const int t = GROUP_MAJOR ? ci % TILES : ci / GMAX;
+    const int u = GROUP_MAJOR ? ci / TILES : ci % GMAX;
+    v4f (&at)[MS] = acc[GROUP_MAJOR ? t : 0];
     if (ci + PD < CH) load_chunk(ci + PD, (ci + PD) % RING);
-    if (u == 0) {
+    if (!GROUP_MAJOR && u == 0) {
 #pragma unroll
-      for (int s = 0; s < MS; ++s) acc[s] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < MS; ++s) at[s] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    if (BF16 && t == 0) {  // first use of group u: quantise its activation
+      float scale;
+      bv[u][0] = quant_group_operand(araw[u], &scale);
+      sa[u][0] = u < gcnt ? scale : 0.f;  // a group past the range adds nothing
     }
     if (LINES && t == 0) {  // first use of group u: its activation lines -> operand
 #pragma unroll
@@ -194,14 +297,14 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     for (int s = 0; s < MS; ++s) {
       const v4f p = mfma_16x16x128_e4m3(wop, bv[u][s]);
       const float sc = sa[u][s] * sw[ci % RING];
-      acc[s][0] = fmaf(sc, p[0], acc[s][0]);
-      acc[s][1] = fmaf(sc, p[1], acc[s][1]);
-      acc[s][2] = fmaf(sc, p[2], acc[s][2]);
-      acc[s][3] = fmaf(sc, p[3], acc[s][3]);
+      at[s][0] = fmaf(sc, p[0], at[s][0]);
+      at[s][1] = fmaf(sc, p[1], at[s][1]);
+      at[s][2] = fmaf(sc, p[2], at[s][2]);
+      at[s][3] = fmaf(sc, p[3], at[s][3]);
     }
     if (u == GMAX - 1) {
 #pragma unroll
-      for (int s = 0; s < MS; ++s) red[wave][t][s][lane] = acc[s];
+      for (int s = 0; s < MS; ++s) red[wave][t][s][lane] = at[s];
     }
   }
   __syncthreads();

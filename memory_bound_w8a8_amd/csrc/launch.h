@@ -18,9 +18,15 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                              const void* wq, const float* ws, void* c, hipStream_t stream);
 
-// Weight-only (bf16 activation) streaming kernel, 1 <= m <= 16 and K/128
-// groups within the instance table (w8a16_supported).
-bool w8a16_supported(int64_t m, int64_t n, int64_t k);
+// The small-M entry points below serve 1 <= m <= 16 and K/128 groups within
+// the streaming instance table.
+bool small_m_supported(int64_t m, int64_t n, int64_t k);
+
+// Activation quantisation fused into the streaming GEMM (bf16 activation in).
+hipError_t launch_gemm_fused(int64_t m, int64_t n, int64_t k, const void* a, const void* wq, const float* ws, void* c,
+                             hipStream_t stream);
+
+// Weight-only (bf16 activation) streaming kernel.
 hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, const void* wq, const float* ws, void* c,
                              hipStream_t stream);
 

@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert _declared() == {"fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_path",
-                           "fp8bq_gemm_forced", "fp8bq_gemm_w8a16", "fp8bq_status_string"}
+                           "fp8bq_gemm_forced", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16", "fp8bq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(fp8bq):
@@ -116,6 +116,20 @@ def test_w8a16_errors(fp8bq):
     assert L.fp8bq_gemm_w8a16(1, 4, 128, p, p, p, p + 2, None) == -3
 
 
+def test_fused_errors(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    assert L.fp8bq_gemm_fused(-1, 4, 128, p, p, p, p, None) == -2
+    assert L.fp8bq_gemm_fused(1, 4, 100, p, p, p, p, None) == -2
+    assert L.fp8bq_gemm_fused(17, 4, 128, p, p, p, p, None) == -2
+    assert L.fp8bq_gemm_fused(1, 4, 9216 + 128, p, p, p, p, None) == -2
+    assert L.fp8bq_gemm_fused(0, 4, 128, None, None, None, None, None) == 0
+    assert L.fp8bq_gemm_fused(1, 4, 128, None, p, p, p, None) == -1
+    assert L.fp8bq_gemm_fused(1, 4, 128, p, p, p, None, None) == -1
+    assert L.fp8bq_gemm_fused(1, 4, 128, p + 2, p, p, p, None) == -3
+    assert L.fp8bq_gemm_fused(1, 4, 128, p, p, p + 1, p, None) == -3
+
+
 def test_gemm_path_dispatch_by_explicit_m_ranges(fp8bq):
     L = fp8bq.lib()
     assert L.fp8bq_gemm_path(0, 17408, 5120) == fp8bq.PATH_NONE
@@ -135,6 +149,7 @@ def test_device_error_without_gpu(fp8bq):
     assert L.fp8bq_gemm(1, 4, 128, p, p, p, p, p, None) == -4
     assert L.fp8bq_quant_act(1, 128, p, p, p, None) == -4
     assert L.fp8bq_gemm_w8a16(1, 4, 128, p, p, p, p, None) == -4
+    assert L.fp8bq_gemm_fused(1, 4, 128, p, p, p, p, None) == -4
 
 
 def test_binding_rejects_cpu_tensors(fp8bq):
