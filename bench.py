@@ -5,10 +5,13 @@
 Workload: the decode and speculative-verify shapes M = 1..8 on the largest
 logged weight shape N = 17408, K = 5120 (page 2, ownding.com L20 report,
 section 8). One step is one pass of the whole hot path over that workload:
-for every M, quantise the activation (fp8bq_quant_act) and run the
-block-FP8 GEMM (fp8bq_gemm). Inputs are resident in HBM before timing. The
-weights rotate over enough distinct copies (>= 1 GiB) that no call finds its
-89 MB weight in the 256 MB Infinity Cache, so every GEMM reads W from HBM.
+for every M, the per-token activation quantisation and the block-FP8 GEMM,
+run as one launch (fp8bq_gemm_fused, bitwise the result of fp8bq_quant_act
+followed by fp8bq_gemm). The two-call form and the weight-only path
+(fp8bq_gemm_w8a16) are timed on the same workload beside it. Inputs are
+resident in HBM before timing. The weights rotate over enough distinct
+copies (>= 1 GiB) that no call finds its 89 MB weight in the 256 MB
+Infinity Cache, so every GEMM reads W from HBM.
 
 Printed: one JSON line with the step throughput (algorithmic bytes per step
 / step time, GB/s), per-M microseconds per call from HIP events on the
@@ -55,9 +58,9 @@ def quant_bytes(m, k):
     return 2 * m * k + m * k + 4 * m * (k // 128)
 
 
-def w8a16_bytes(m, n, k):
-    """Algorithmic bytes of one weight-only call: W codes + W scales + bf16
-    activation + C (bf16)."""
+def bf16_act_bytes(m, n, k):
+    """Algorithmic bytes of one call that takes the bf16 activation (fused
+    or weight-only): W codes + W scales + bf16 activation + C (bf16)."""
     g = k // 128
     return n * k + 4 * ((n + 127) // 128) * g + 2 * m * k + 2 * m * n
 
@@ -77,7 +80,7 @@ def kernel_source_digest():
 def stored_traffic(digest):
     """HBM traffic per GEMM launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", "gemm_rows_decode_M1-8_N17408_K5120_pmc.txt")
+    path = os.path.join(ROOT, "profiles", "gemm_rows_fused_decode_M1-8_N17408_K5120_pmc.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -248,7 +251,7 @@ def cpu_baseline(budget_s=20.0, rows=4096):
                 a_q, a_s = quant_act_ref(acts[m])
                 gemm_ref(a_q, a_s, w_q, w_s)
             t_total += time.perf_counter() - t0
-            bytes_total += sum(gemm_bytes(m, rows, K) + quant_bytes(m, K) for m in MS)
+            bytes_total += sum(bf16_act_bytes(m, rows, K) for m in MS)
             passes += 1
     return {
         "value": round(bytes_total / t_total / 1e9, 4),
@@ -264,7 +267,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--kernel-reps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=3465 prefill GEMM timing")
@@ -298,18 +301,17 @@ def main():
           file=sys.stderr, flush=True)
     plan = Plan(copies)
 
-    for _ in range(args.warmup):
-        plan.step()
-    torch.cuda.synchronize()
-
     print(f"bench: timing {args.steps} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        plan.step_fused()
+    torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(plan.stream)
     for _ in range(args.steps):
-        plan.step()
+        plan.step_fused()
     e1.record(plan.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -328,27 +330,29 @@ def main():
         torch.cuda.synchronize()
         return ea.elapsed_time(eb) / args.steps
 
-    # the same workload with quantisation fused into the GEMM, and through
-    # the weight-only entry point: one launch per M each
-    ms_fused = time_steps(plan.step_fused)
+    # the same workload as two calls per M (quant_act, gemm), and through
+    # the weight-only entry point (one launch per M)
+    ms_unfused = time_steps(plan.step)
     ms_w8a16 = time_steps(plan.step_w8a16)
-    w8a16_step_bytes = sum(w8a16_bytes(m, N, K) for m in MS)
+    fused_step_bytes = sum(bf16_act_bytes(m, N, K) for m in MS)
 
     kt = time_kernels(plan, args.kernel_reps)
-    step_bytes = sum(gemm_bytes(m, N, K) + quant_bytes(m, K) for m in MS)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    unfused_step_bytes = sum(gemm_bytes(m, N, K) + quant_bytes(m, K) for m in MS)
+    value = fused_step_bytes / (ms_per_step * 1e-3) / 1e9
 
     per_m = []
     for m in MS:
-        us = kt[("gemm", m)]
-        gbs = gemm_bytes(m, N, K) / (us * 1e-6) / 1e9
-        per_m.append({"M": m, "gemm_us": round(us, 3), "gemm_GBps": round(gbs, 1),
-                      "gemm_pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "quant_act_us": round(kt[("quant", m)], 3),
-                      "fused_us": round(kt[("fused", m)], 3),
+        us = kt[("fused", m)]
+        gbs = bf16_act_bytes(m, N, K) / (us * 1e-6) / 1e9
+        per_m.append({"M": m, "fused_us": round(us, 3), "fused_GBps": round(gbs, 1),
+                      "fused_pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                      "gemm_us": round(kt[("gemm", m)], 3),
+                      "gemm_GBps": round(gemm_bytes(m, N, K) / (kt[("gemm", m)] * 1e-6) / 1e9, 1),
+                      "quant_act_us": round(kt[("quant", m)], 3),
                       "w8a16_us": round(kt[("w8a16", m)], 3),
-                      "w8a16_GBps": round(w8a16_bytes(m, N, K) / (kt[("w8a16", m)] * 1e-6) / 1e9, 1)})
-    g_bytes = sum(gemm_bytes(m, N, K) for m in MS)
-    g_time = sum(kt[("gemm", m)] for m in MS) * 1e-6
+                      "w8a16_GBps": round(bf16_act_bytes(m, N, K) / (kt[("w8a16", m)] * 1e-6) / 1e9, 1)})
+    g_bytes = sum(bf16_act_bytes(m, N, K) for m in MS)
+    g_time = sum(kt[("fused", m)] for m in MS) * 1e-6
     achieved = g_bytes / g_time / 1e9
     digest = kernel_source_digest()
     traffic = stored_traffic(digest)
@@ -367,8 +371,9 @@ def main():
         "dtype": "fp8",
         "data": "synthetic",
         "config": {
-            "workload": "decode/verify M=1..8 x (N=17408, K=5120): quant_act + block-FP8 gemm per M",
-            "M": MS, "N": N, "K": K, "weight_copies": copies, "step_bytes": step_bytes,
+            "workload": "decode/verify M=1..8 x (N=17408, K=5120): per-token activation quantisation + block-FP8 "
+                        "gemm per M, one fused launch each (fp8bq_gemm_fused)",
+            "M": MS, "N": N, "K": K, "weight_copies": copies, "step_bytes": fused_step_bytes,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 1),
             "parallelism": "single GPU",
         },
@@ -380,24 +385,23 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "gemm_rows_kernel<16, 8, 5, 5, 6, false> (the M=1..8 launches; HIP events on the launch "
-                      "stream around back-to-back launches)",
+            "kernel": "gemm_rows_kernel<16, 8, 5, 5, 6, 2> (fused quantisation + GEMM, the M=1..8 launches; HIP "
+                      "events on the launch stream around back-to-back launches)",
         },
-        "fused": {
-            "path": "fp8bq_gemm_fused (activation quantisation inside the block-FP8 GEMM, bitwise the two-call "
-                    "result), one launch per M, same weights and activations",
-            "ms_per_step": round(ms_fused, 5),
-            "value": round(w8a16_step_bytes / (ms_fused * 1e-3) / 1e9, 1),
+        "unfused": {
+            "path": "fp8bq_quant_act then fp8bq_gemm per M (two launches), same weights and activations",
+            "ms_per_step": round(ms_unfused, 5),
+            "value": round(unfused_step_bytes / (ms_unfused * 1e-3) / 1e9, 1),
             "unit": "GB/s",
-            "step_bytes": w8a16_step_bytes,
+            "step_bytes": unfused_step_bytes,
         },
         "w8a16": {
             "path": "fp8bq_gemm_w8a16 (bf16 activation x block-FP8 weight, no activation quantisation), "
                     "one launch per M, same weights and activations",
             "ms_per_step": round(ms_w8a16, 5),
-            "value": round(w8a16_step_bytes / (ms_w8a16 * 1e-3) / 1e9, 1),
+            "value": round(fused_step_bytes / (ms_w8a16 * 1e-3) / 1e9, 1),
             "unit": "GB/s",
-            "step_bytes": w8a16_step_bytes,
+            "step_bytes": fused_step_bytes,
         },
         "wall_s_timed": round(wall, 3),
         "kernel_source_digest": digest,
