@@ -227,6 +227,60 @@ def prefill(plan, reps=20):
     return out
 
 
+SWEEP_M = [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 33, 48, 64, 65, 96, 128, 129, 192, 256, 384, 512, 1024,
+           2048, 3465, 4096]
+
+
+def m_sweep():
+    """fp8bq_gemm over an M grid on the five logged shapes: microseconds per
+    call (HIP events on the launch stream, weights rotating over >= 1 GiB of
+    copies), GB/s of algorithmic bytes and TFLOP/s. The dispatch boundaries
+    (8/9, 16/17, 32/33, 64/65, 128/129) are in the grid on purpose."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    s = ctypes.c_void_p(stream.cuda_stream)
+    L = fp8bq.lib()
+    g = torch.Generator(device=dev)
+    rows = []
+    mmax = max(SWEEP_M)
+    for n, k in workloads.SHAPES:
+        copies = max(2, -(-(1 << 30) // (n * k)))
+        ws = []
+        for i in range(copies):
+            g.manual_seed(500 + i)
+            w32 = torch.randn((n, k), generator=g, device=dev, dtype=torch.float32).mul_(0.02)
+            ws.append(fp8bq.quant_weight(w32))
+            del w32
+        g.manual_seed(77)
+        a = torch.randn((mmax, k), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        aq, as_ = fp8bq.quant_act(a)
+        c = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
+        for m in SWEEP_M:
+            def call(i):
+                wq, wsc = ws[i % copies]
+                st = L.fp8bq_gemm(m, n, k, aq.data_ptr(), as_.data_ptr(), wq.data_ptr(), wsc.data_ptr(), c.data_ptr(), s)
+                if st:
+                    raise fp8bq.Fp8bqError("fp8bq_gemm", st)
+            reps = 8 * copies if m <= 256 else 12
+            for i in range(reps):
+                call(i)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                call(i)
+            e1.record(stream)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            rows.append({"N": n, "K": k, "M": m, "path": fp8bq.PATH_NAMES[L.fp8bq_gemm_path(m, n, k)],
+                         "us": round(us, 2), "GBps": round(gemm_bytes(m, n, k) / (us * 1e-6) / 1e9, 1),
+                         "TFLOPs": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)})
+            print(f"bench: sweep N={n} K={k} M={m}: {us:.2f} us", file=sys.stderr, flush=True)
+        del ws, a, aq, as_, c
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(budget_s=20.0, rows=4096):
     """The CPU oracle (numpy, fp64 GEMM) on a bounded sample: quantise the
     activation and compute the GEMM for M = 1..8 against the first `rows`
@@ -271,6 +325,8 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=3465 prefill GEMM timing")
+    ap.add_argument("--m-sweep", action="store_true",
+                    help="instead of the benchmark, time fp8bq_gemm over an M grid on the five shapes (one JSON line)")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a dispatch of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -284,6 +340,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.m_sweep:
+        print(json.dumps({"metric": "fp8bq_gemm us/call over M", "data": "synthetic", "rows": m_sweep(),
+                          "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
 
     if args.calibration_copy_mb > 0:
         nbytes = args.calibration_copy_mb << 20
