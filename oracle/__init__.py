@@ -28,6 +28,9 @@ Modules:
   sampled output positions.
 * ``w8a16`` -- the weight-only variant (bf16 activation x block-FP8 weight,
   page 1's W8A16 backend), fp64, whole or sampled.
+* ``scoring`` -- two-stage vocabulary scoring: exact top-k of coarse logits
+  and exact fp64 rescoring of the survivors (page 1's FP8-screen,
+  BF16-score scheme).
 
 Every function is pinned by ``-m "not gpu"`` tests against something other
 than itself (torch's float8_e4m3fn casts, exact rational brute force, closed
@@ -38,6 +41,7 @@ from .e4m3 import E4M3_MAX, e4m3_decode, e4m3_encode_rne, e4m3_values
 from .quant import quant_act_ref, quant_weight_ref
 from .gemm import gemm_ref, gemm_ref_at
 from .w8a16 import gemm_w8a16_ref, gemm_w8a16_ref_at
+from .scoring import bf16_key, rescore_ref, topk_ref
 
 __all__ = [
     "E4M3_MAX",
@@ -50,4 +54,7 @@ __all__ = [
     "gemm_ref_at",
     "gemm_w8a16_ref",
     "gemm_w8a16_ref_at",
+    "bf16_key",
+    "topk_ref",
+    "rescore_ref",
 ]
