@@ -168,6 +168,70 @@ int fp8bq_gemm_fused(int64_t M, int64_t N, int64_t K, const void *A_bf16, const 
 int fp8bq_gemm_w8a16(int64_t M, int64_t N, int64_t K, const void *A_bf16, const void *W_fp8,
                      const float *W_scales, void *C_bf16, void *stream);
 
+/*
+ * Two-stage vocabulary scoring (page 1, SmartX blog, "single-stream
+ * optimisation": the draft head reads the whole vocabulary projection every
+ * step; all candidates are screened with FP8 scores and only the survivors
+ * are scored exactly in BF16). Stage 1 is fp8bq_gemm / fp8bq_gemm_fused of
+ * the hidden state with the FP8 vocabulary projection, giving coarse bf16
+ * logits [M, V]; stage 2 is fp8bq_topk_bf16; stage 3 is fp8bq_rescore_bf16
+ * against the BF16 projection.
+ *
+ * Order (the pages give none): bf16 values compare by their bit pattern
+ * mapped to a monotone unsigned key (negative patterns inverted, positive
+ * ones with the top bit set; so -0 ranks just below +0, and NaN patterns
+ * rank by their bits like any other), equal keys by the lower index.
+ */
+
+/*
+ * Bytes of device workspace fp8bq_topk_bf16 needs for (M, V, k), or a
+ * negative status for sizes it rejects. The size depends on M, V and k only.
+ */
+int64_t fp8bq_topk_workspace_bytes(int64_t M, int64_t V, int64_t k);
+
+/*
+ * Exact top-k of each row of bf16 logits.
+ *
+ *   logits_bf16  [M, V] bf16, read.
+ *   workspace    device scratch of at least workspace_bytes >=
+ *                fp8bq_topk_workspace_bytes(M, V, k) bytes; contents on
+ *                entry are ignored, on return unspecified. Calls that share
+ *                a workspace must be ordered (same stream).
+ *   idx_out      [M, k] int32, written: the k best entries of each row in
+ *                order (best first), by the order above.
+ *   val_bf16_out [M, k] bf16, written: their logit bit patterns.
+ * Bit-exact (an order, no arithmetic); deterministic.
+ * M == 0 is a quick return. Errors: k < 1, k > 256 or k > V; V >= 2^31;
+ * M*V > 2^40; more than 2^21 chunks of 4096 logits in all (M * ceil(V /
+ * 4096)); workspace_bytes too small; NULL pointer; logits, workspace or
+ * val_bf16_out not 16-B aligned, idx_out not 4-B aligned; device not gfx950.
+ */
+int fp8bq_topk_bf16(int64_t M, int64_t V, int64_t k, const void *logits_bf16, void *workspace,
+                    int64_t workspace_bytes, int32_t *idx_out, void *val_bf16_out, void *stream);
+
+/*
+ * Exact scores of the survivors and each row's pick.
+ *
+ *   h_bf16     [M, K] bf16 hidden states, read.
+ *   W_bf16     [V, K] bf16 vocabulary projection, read (rows idx only).
+ *   idx        [M, k] int32 survivor indices, read (e.g. fp8bq_topk_bf16's).
+ *   scores_out [M, k] fp32, written: scores_out[m, j] =
+ *              sum_k h[m, k] * W[idx[m, j], k], products exact in fp32, fp32
+ *              accumulation in a fixed order (bitwise repeatable); NaN for an
+ *              index outside [0, V), whose row is not read.
+ *   pick_out   [M] int32, written: the index of the survivor with the largest
+ *              score (ties to the lower index); NaN scores are never picked;
+ *              -1 when all of a row's scores are NaN.
+ * M == 0 is a quick return; K == 0 scores 0. Errors: k < 1; K % 8 != 0;
+ * V >= 2^31; M*K, V*K or M*k > 2^40; more than 2^21 rows or survivor groups
+ * of 16; NULL pointer (h_bf16 and W_bf16 may be NULL when K == 0); h_bf16 or
+ * W_bf16 not 16-B aligned, idx, scores_out or pick_out not 4-B aligned;
+ * device not gfx950.
+ */
+int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void *h_bf16,
+                       const void *W_bf16, const int32_t *idx, float *scores_out,
+                       int32_t *pick_out, void *stream);
+
 /* Human-readable name of a status code; never NULL. */
 const char *fp8bq_status_string(int status);
 

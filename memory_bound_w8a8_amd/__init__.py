@@ -8,6 +8,11 @@ is missing or cannot run, the calls raise.
     a_q, a_s = quant_act(a)              # a: bf16 [M, K] on the GPU
     w_q, w_s = quant_weight(w)           # w: fp32 [N, K] on the GPU
     c = gemm(a_q, a_s, w_q, w_s)         # c: bf16 [M, N]
+
+Two-stage vocabulary scoring (coarse FP8 logits, exact top-k, exact BF16
+rescoring of the survivors):
+
+    pick, idx, scores = two_stage(h, w_q, w_s, w_bf16, k)
 """
 
 import ctypes
@@ -31,6 +36,9 @@ EXPORTS = (
     "fp8bq_gemm_forced",
     "fp8bq_gemm_fused",
     "fp8bq_gemm_w8a16",
+    "fp8bq_topk_workspace_bytes",
+    "fp8bq_topk_bf16",
+    "fp8bq_rescore_bf16",
     "fp8bq_status_string",
 )
 
@@ -61,9 +69,14 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_gemm_path.argtypes = [i64, i64, i64]
         L.fp8bq_gemm_w8a16.argtypes = [i64, i64, i64, vp, vp, fp, vp, vp]
         L.fp8bq_gemm_fused.argtypes = [i64, i64, i64, vp, vp, fp, vp, vp]
+        L.fp8bq_topk_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fp8bq_topk_workspace_bytes.restype = i64
+        L.fp8bq_topk_bf16.argtypes = [i64, i64, i64, vp, vp, i64, vp, vp, vp]
+        L.fp8bq_rescore_bf16.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.fp8bq_status_string.argtypes = [ctypes.c_int]
         L.fp8bq_status_string.restype = ctypes.c_char_p
-        for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path"):
+        for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path",
+                     "fp8bq_gemm_w8a16", "fp8bq_gemm_fused", "fp8bq_topk_bf16", "fp8bq_rescore_bf16"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -210,3 +223,66 @@ def gemm_path(m: int, n: int, k: int) -> int:
     if st < 0:
         raise Fp8bqError("fp8bq_gemm_path", st)
     return st
+
+
+def topk_workspace_bytes(m: int, v: int, k: int) -> int:
+    """Device workspace bytes topk() needs for (M, V, k); raises on sizes the
+    library rejects."""
+    st = lib().fp8bq_topk_workspace_bytes(int(m), int(v), int(k))
+    if st < 0:
+        raise Fp8bqError("fp8bq_topk_workspace_bytes", st)
+    return st
+
+
+def topk(logits: torch.Tensor, k: int, workspace: torch.Tensor = None):
+    """Exact top-k of each row of bf16 logits [M, V] (1 <= k <= 256): int32
+    indices [M, k], best first (equal values: lower index first), and their
+    bf16 values. `workspace` (uint8, on the device) is allocated if absent."""
+    _need(logits, "logits", torch.bfloat16, 2)
+    m, v = logits.shape
+    need = topk_workspace_bytes(m, v, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=logits.device)
+    else:
+        _need(workspace, "workspace", torch.uint8, 1)
+    idx = torch.empty((m, k), dtype=torch.int32, device=logits.device)
+    val = torch.empty((m, k), dtype=torch.bfloat16, device=logits.device)
+    with torch.cuda.device(logits.device):
+        st = lib().fp8bq_topk_bf16(m, v, int(k), _ptr(logits), _ptr(workspace), workspace.numel(), _ptr(idx),
+                                   _ptr(val), _stream(logits))
+    _check("fp8bq_topk_bf16", st)
+    return idx, val
+
+
+def rescore(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor):
+    """Exact scores of survivors: h bf16 [M, K], w bf16 [V, K], idx int32
+    [M, k] -> (fp32 scores [M, k], int32 pick [M]: the best survivor, ties to
+    the lower index)."""
+    _need(h, "h", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 2)
+    _need(idx, "idx", torch.int32, 2)
+    m, kdim = h.shape
+    v, k2 = w.shape
+    if k2 != kdim:
+        raise ValueError(f"K mismatch: h has {kdim}, w has {k2}")
+    if idx.shape[0] != m:
+        raise ValueError(f"idx has {idx.shape[0]} rows, h has {m}")
+    k = idx.shape[1]
+    scores = torch.empty((m, k), dtype=torch.float32, device=h.device)
+    pick = torch.empty((m,), dtype=torch.int32, device=h.device)
+    with torch.cuda.device(h.device):
+        st = lib().fp8bq_rescore_bf16(m, kdim, v, k, _ptr(h), _ptr(w), _ptr(idx), _ptr(scores), _ptr(pick),
+                                      _stream(h))
+    _check("fp8bq_rescore_bf16", st)
+    return scores, pick
+
+
+def two_stage(h: torch.Tensor, w_q, w_s, w_bf16: torch.Tensor, k: int, workspace: torch.Tensor = None):
+    """Two-stage vocabulary scoring of hidden states h bf16 [M, K] (M <= 16):
+    coarse logits by the fused block-FP8 GEMM against (w_q, w_s), their exact
+    top-k, exact scores of those k against the bf16 projection w_bf16 [V, K].
+    Returns (pick int32 [M], idx int32 [M, k], scores fp32 [M, k])."""
+    logits = gemm_fused(h, w_q, w_s)
+    idx, _ = topk(logits, k, workspace)
+    scores, pick = rescore(h, w_bf16, idx)
+    return pick, idx, scores

@@ -16,6 +16,9 @@ constexpr int64_t kTiledMaxK = int64_t(1) << 24; // tiled kernel: 32-bit offsets
 constexpr int kMaxDevices = 64;
 constexpr int64_t kSmallMaxM = 16;               // fused and weight-only paths: one 16-token tile
 constexpr int64_t kSmallMaxK = 72 * 128;         // groups within their instance tables
+constexpr int64_t kTopkMaxK = 256;               // survivors per row
+constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;  // vocabulary indices are int32
+constexpr int64_t kMaxGridBlocks = int64_t(1) << 21;   // 1024-thread workgroups in one 1-D grid
 
 // Per-device capability cache: 0 = unknown, 1 = gfx950, -1 = not usable.
 std::atomic<int> g_device_ok[kMaxDevices];
@@ -155,6 +158,43 @@ int fp8bq_gemm_w8a16(int64_t M, int64_t N, int64_t K, const void* A_bf16, const 
   if (K == 0) return launch_status(fp8bq::launch_fill_zero_bf16(M * N, C_bf16, s));
   if (!fp8bq::small_m_supported(M, N, K)) return FP8BQ_ERR_SHAPE;
   return launch_status(fp8bq::launch_gemm_w8a16(M, N, K, A_bf16, W_fp8, W_scales, C_bf16, s));
+}
+
+int64_t fp8bq_topk_workspace_bytes(int64_t M, int64_t V, int64_t k) {
+  if (M < 0 || V < 0 || V > kMaxIndex || k < 1 || k > kTopkMaxK || k > V || !product_ok(M, V)) return FP8BQ_ERR_SHAPE;
+  return fp8bq::topk_workspace_bytes(M, V, k);
+}
+
+int fp8bq_topk_bf16(int64_t M, int64_t V, int64_t k, const void* logits_bf16, void* workspace,
+                    int64_t workspace_bytes, int32_t* idx_out, void* val_bf16_out, void* stream) {
+  if (M < 0 || V < 0 || V > kMaxIndex || k < 1 || k > kTopkMaxK || k > V || !product_ok(M, V)) return FP8BQ_ERR_SHAPE;
+  if (fp8bq::topk_grid_blocks(M, V) > kMaxGridBlocks) return FP8BQ_ERR_SHAPE;
+  if (M == 0) return FP8BQ_OK;
+  if (workspace_bytes < fp8bq::topk_workspace_bytes(M, V, k)) return FP8BQ_ERR_SHAPE;
+  if (logits_bf16 == nullptr || workspace == nullptr || idx_out == nullptr || val_bf16_out == nullptr)
+    return FP8BQ_ERR_NULL;
+  if (!aligned(logits_bf16, 16) || !aligned(workspace, 16) || !aligned(idx_out, 4) || !aligned(val_bf16_out, 16))
+    return FP8BQ_ERR_ALIGN;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(fp8bq::launch_topk(M, V, static_cast<int>(k), logits_bf16, workspace, idx_out, val_bf16_out,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void* h_bf16, const void* W_bf16,
+                       const int32_t* idx, float* scores_out, int32_t* pick_out, void* stream) {
+  if (M < 0 || K < 0 || K % 8 != 0 || V < 0 || V > kMaxIndex || k < 1) return FP8BQ_ERR_SHAPE;
+  if (!product_ok(M, K) || !product_ok(V, K) || !product_ok(M, k)) return FP8BQ_ERR_SHAPE;
+  if (fp8bq::rescore_grid_blocks(M, k) > kMaxGridBlocks || M > kMaxGridBlocks) return FP8BQ_ERR_SHAPE;
+  if (M == 0) return FP8BQ_OK;
+  if (idx == nullptr || scores_out == nullptr || pick_out == nullptr) return FP8BQ_ERR_NULL;
+  if (K > 0 && (h_bf16 == nullptr || W_bf16 == nullptr)) return FP8BQ_ERR_NULL;
+  if (!aligned(idx, 4) || !aligned(scores_out, 4) || !aligned(pick_out, 4)) return FP8BQ_ERR_ALIGN;
+  if (K > 0 && (!aligned(h_bf16, 16) || !aligned(W_bf16, 16))) return FP8BQ_ERR_ALIGN;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(fp8bq::launch_rescore(M, K, V, k, h_bf16, W_bf16, idx, scores_out, pick_out,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 const char* fp8bq_status_string(int status) {

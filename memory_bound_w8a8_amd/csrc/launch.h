@@ -30,6 +30,17 @@ hipError_t launch_gemm_fused(int64_t m, int64_t n, int64_t k, const void* a, con
 hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, const void* wq, const float* ws, void* c,
                              hipStream_t stream);
 
+// Two-stage vocabulary scoring (scoring.hip). topk: 1 <= k <= 256, k <= v;
+// the workspace holds topk_workspace_bytes(m, v, k) bytes; the grids hold
+// topk_grid_blocks / rescore_grid_blocks workgroups of 1024 threads.
+int64_t topk_workspace_bytes(int64_t m, int64_t v, int64_t k);
+int64_t topk_grid_blocks(int64_t m, int64_t v);
+int64_t rescore_grid_blocks(int64_t m, int64_t k);
+hipError_t launch_topk(int64_t m, int64_t v, int k, const void* logits, void* workspace, int* idx, void* val,
+                       hipStream_t stream);
+hipError_t launch_rescore(int64_t m, int64_t kdim, int64_t v, int64_t k, const void* h, const void* w,
+                          const int* idx, float* scores, int* pick, hipStream_t stream);
+
 // C = 0 (used for K == 0).
 hipError_t launch_fill_zero_bf16(int64_t count, void* c, hipStream_t stream);
 

@@ -25,12 +25,13 @@ def fp8bq():
 
 def _declared():
     text = open(HEADER).read()
-    return set(re.findall(r"^\s*(?:int|const char \*)\s*(fp8bq_\w+)\s*\(", text, flags=re.M))
+    return set(re.findall(r"^\s*(?:int|int64_t|const char \*)\s*(fp8bq_\w+)\s*\(", text, flags=re.M))
 
 
 def test_header_declares_the_abi():
     assert _declared() == {"fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_path",
-                           "fp8bq_gemm_forced", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16", "fp8bq_status_string"}
+                           "fp8bq_gemm_forced", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16", "fp8bq_topk_workspace_bytes",
+                           "fp8bq_topk_bf16", "fp8bq_rescore_bf16", "fp8bq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(fp8bq):
@@ -130,6 +131,66 @@ def test_fused_errors(fp8bq):
     assert L.fp8bq_gemm_fused(1, 4, 128, p, p, p + 1, p, None) == -3
 
 
+def test_topk_workspace_size(fp8bq):
+    L = fp8bq.lib()
+    # first level: one list of k per 4096 logits; second: one per 4096 / p lists
+    # (p = power of two >= k), 8 bytes an entry
+    for m, v, k in ((1, 152064, 64), (4, 152064, 50), (3, 4096, 256), (2, 4097, 1), (1, 10, 10), (16, 1 << 20, 7)):
+        p = 1 << (k - 1).bit_length()
+        l0 = -(-v // 4096)
+        l1 = -(-l0 // (4096 // p))
+        assert L.fp8bq_topk_workspace_bytes(m, v, k) == (l0 + l1) * m * k * 8, (m, v, k)
+    assert L.fp8bq_topk_workspace_bytes(0, 100, 5) == 8 * 0
+    assert L.fp8bq_topk_workspace_bytes(1, 100, 0) == -2
+    assert L.fp8bq_topk_workspace_bytes(1, 100, 257) == -2
+    assert L.fp8bq_topk_workspace_bytes(1, 100, 101) == -2
+    assert L.fp8bq_topk_workspace_bytes(-1, 100, 5) == -2
+    assert L.fp8bq_topk_workspace_bytes(1, 1 << 31, 5) == -2
+
+
+def test_topk_errors(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    ws = L.fp8bq_topk_workspace_bytes(2, 1000, 8)
+    assert L.fp8bq_topk_bf16(2, 1000, 0, p, p, ws, p, p, None) == -2
+    assert L.fp8bq_topk_bf16(2, 1000, 257, p, p, ws, p, p, None) == -2
+    assert L.fp8bq_topk_bf16(2, 7, 8, p, p, ws, p, p, None) == -2  # k > V
+    assert L.fp8bq_topk_bf16(-1, 1000, 8, p, p, ws, p, p, None) == -2
+    assert L.fp8bq_topk_bf16(2, 1 << 31, 8, p, p, ws, p, p, None) == -2
+    assert L.fp8bq_topk_bf16(1 << 12, 1 << 22, 8, p, p, 1 << 40, p, p, None) == -2  # 2^22 chunks
+    assert L.fp8bq_topk_bf16(2, 1000, 8, p, p, ws - 1, p, p, None) == -2
+    assert L.fp8bq_topk_bf16(0, 1000, 8, None, None, 0, None, None, None) == 0
+    assert L.fp8bq_topk_bf16(2, 1000, 8, None, p, ws, p, p, None) == -1
+    assert L.fp8bq_topk_bf16(2, 1000, 8, p, None, ws, p, p, None) == -1
+    assert L.fp8bq_topk_bf16(2, 1000, 8, p, p, ws, None, p, None) == -1
+    assert L.fp8bq_topk_bf16(2, 1000, 8, p, p, ws, p, None, None) == -1
+    assert L.fp8bq_topk_bf16(2, 1000, 8, p + 2, p, ws, p, p, None) == -3
+    assert L.fp8bq_topk_bf16(2, 1000, 8, p, p + 8, ws, p, p, None) == -3
+    assert L.fp8bq_topk_bf16(2, 1000, 8, p, p, ws, p + 2, p, None) == -3
+    assert L.fp8bq_topk_bf16(2, 1000, 8, p, p, ws, p, p + 2, None) == -3
+
+
+def test_rescore_errors(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 0, p, p, p, p, p, None) == -2  # k < 1
+    assert L.fp8bq_rescore_bf16(1, 60, 100, 4, p, p, p, p, p, None) == -2  # K % 8
+    assert L.fp8bq_rescore_bf16(-1, 64, 100, 4, p, p, p, p, p, None) == -2
+    assert L.fp8bq_rescore_bf16(1, 64, 1 << 31, 4, p, p, p, p, p, None) == -2
+    assert L.fp8bq_rescore_bf16(1 << 22, 64, 100, 4, p, p, p, p, p, None) == -2  # too many rows
+    assert L.fp8bq_rescore_bf16(0, 64, 100, 4, None, None, None, None, None, None) == 0
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, None, p, p, p, p, None) == -1
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, None, p, p, p, None) == -1
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p, None, p, p, None) == -1
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p, p, None, p, None) == -1
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p, p, p, None, None) == -1
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p + 8, p, p, p, p, None) == -3
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p + 8, p, p, p, None) == -3
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p, p + 2, p, p, None) == -3
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p, p, p + 2, p, None) == -3
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p, p, p, p + 2, None) == -3
+
+
 def test_gemm_path_dispatch_by_explicit_m_ranges(fp8bq):
     L = fp8bq.lib()
     assert L.fp8bq_gemm_path(0, 17408, 5120) == fp8bq.PATH_NONE
@@ -150,6 +211,8 @@ def test_device_error_without_gpu(fp8bq):
     assert L.fp8bq_quant_act(1, 128, p, p, p, None) == -4
     assert L.fp8bq_gemm_w8a16(1, 4, 128, p, p, p, p, None) == -4
     assert L.fp8bq_gemm_fused(1, 4, 128, p, p, p, p, None) == -4
+    assert L.fp8bq_topk_bf16(1, 100, 5, p, p, L.fp8bq_topk_workspace_bytes(1, 100, 5), p, p, None) == -4
+    assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p, p, p, p, None) == -4
 
 
 def test_binding_rejects_cpu_tensors(fp8bq):

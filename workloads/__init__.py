@@ -17,6 +17,14 @@ pages' shapes replace them:
 * the tiny case (M=1, N=512, K=1024) uses one generator seeded 0, drawing W
   first and then A, with no outliers.
 
+Two-stage vocabulary scoring (page 1, section "single-stream optimisation")
+runs the same GEMM against a vocabulary-sized projection. The pages print
+neither the vocabulary size nor the survivor count: V = 152064 (a
+Qwen-family vocabulary padded to a multiple of 128) and k = 64 stand in.
+Its inputs are the hidden state (an activation of width K = 5120), the
+projection W (drawn like any weight, bf16 copy by RNE) and, for the
+selection and rescoring stages alone, seeded logits and survivor indices.
+
 Seeds: W for shape (N, K) is drawn one 128-row block at a time, block b
 from ``numpy.random.default_rng([0, N, K, b])`` (so a test can rebuild any
 row block without drawing the whole matrix); A for (M, N, K) comes from
@@ -31,6 +39,9 @@ SHAPES = [(17408, 5120), (5120, 3072), (5120, 8704), (7168, 5120), (8192, 5120)]
 TINY = (1, 512, 1024)  # (M, N, K)
 PREFILL_M = 3465  # prompt length of page 2's output test (section 4.2)
 PREFILL_SHAPES = [(17408, 5120), (5120, 8704)]
+VOCAB = 152064  # stand-in vocabulary size
+SURVIVORS = 64  # stand-in survivor count
+HIDDEN = 5120
 OUTLIER_FRACTION = 0.001
 OUTLIER_FACTOR = 20.0
 
@@ -90,3 +101,27 @@ def random_scales(shape, seed: int, lo: float = 2.0 ** -12, hi: float = 2.0 ** -
     """Positive fp32 scales, log-uniform in [lo, hi)."""
     rng = np.random.default_rng(seed)
     return np.exp(rng.uniform(np.log(lo), np.log(hi), size=shape)).astype(np.float32)
+
+
+def logit_bits(m: int, v: int, kind: str, seed: int) -> np.ndarray:
+    """bf16 bit patterns uint16 [M, V] for the selection stage.
+
+    kind "normal": bf16 of 3 N(0, 1) (bf16's 8-bit mantissa makes equal
+    values common); "ties": 5 distinct values, mostly equal; "bits": every
+    16-bit pattern equally likely (signed zeros, infinities, NaN patterns)."""
+    rng = np.random.default_rng([2, m, v, seed])
+    if kind == "normal":
+        x = (3.0 * rng.standard_normal((m, v))).astype(np.float32)
+        return to_bf16(x).view(torch.int16).numpy().view(np.uint16)
+    if kind == "ties":
+        vals = np.array([-1.5, -0.0, 0.0, 0.75, 2.0], dtype=np.float32)
+        return to_bf16(rng.choice(vals, size=(m, v))).view(torch.int16).numpy().view(np.uint16)
+    if kind == "bits":
+        return rng.integers(0, 1 << 16, size=(m, v), dtype=np.int64).astype(np.uint16)
+    raise ValueError(kind)
+
+
+def survivor_indices(m: int, v: int, k: int, seed: int) -> np.ndarray:
+    """int32 [M, k]: per row, k distinct vocabulary indices in random order."""
+    rng = np.random.default_rng([3, m, v, k, seed])
+    return np.stack([rng.choice(v, size=k, replace=False) for _ in range(m)]).astype(np.int32)
