@@ -16,8 +16,10 @@ Infinity Cache, so every GEMM reads W from HBM.
 Printed: one JSON line with the step throughput (algorithmic bytes per step
 / step time, GB/s), per-M microseconds per call from HIP events on the
 launch stream, the roofline of the dominant kernel (the GEMM), the prefill
-GEMMs (M = 3465) against the FP8 MFMA peak, and the CPU oracle timed on a
-bounded sample of the same workload.
+GEMMs (M = 3465) against the FP8 MFMA peak, two-stage vocabulary scoring
+(coarse FP8 logits, exact top-64, exact bf16 rescoring; V = 152064 stand-in,
+K = 5120) per stage and per M, and the CPU oracle timed on a bounded sample
+of the same workload.
 """
 
 import argparse
@@ -227,6 +229,86 @@ def prefill(plan, reps=20):
     return out
 
 
+def two_stage(reps=50):
+    """Two-stage vocabulary scoring (page 1, "single-stream optimisation"):
+    coarse logits from the fused block-FP8 GEMM against the FP8 vocabulary
+    projection (V = 152064 stand-in, K = 5120), exact top-64
+    (fp8bq_topk_bf16), exact bf16 rescoring of the 64 survivors
+    (fp8bq_rescore_bf16). Per M: microseconds of each stage and of the whole
+    pipeline (HIP events on the launch stream around `reps` back-to-back
+    calls, buffers preallocated), and, for context, torch's bf16 matmul of
+    the full projection (the one-stage read the scheme replaces)."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    L = fp8bq.lib()
+    v, k, kk = workloads.VOCAB, workloads.HIDDEN, workloads.SURVIVORS
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    w32 = torch.randn((v, k), generator=g, device=dev, dtype=torch.float32).mul_(0.02)
+    wq, ws = fp8bq.quant_weight(w32)
+    wbf = w32.to(torch.bfloat16)
+    del w32
+    out = []
+    for m in (1, 4, 8, 16):
+        g.manual_seed(m)
+        h = torch.randn((m, k), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        logits = torch.empty((m, v), dtype=torch.bfloat16, device=dev)
+        wsb = fp8bq.topk_workspace_bytes(m, v, kk)
+        work = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        idx = torch.empty((m, kk), dtype=torch.int32, device=dev)
+        val = torch.empty((m, kk), dtype=torch.bfloat16, device=dev)
+        scores = torch.empty((m, kk), dtype=torch.float32, device=dev)
+        pick = torch.empty((m,), dtype=torch.int32, device=dev)
+
+        def coarse():
+            st = L.fp8bq_gemm_fused(m, v, k, h.data_ptr(), wq.data_ptr(), ws.data_ptr(), logits.data_ptr(), s)
+            if st:
+                raise fp8bq.Fp8bqError("fp8bq_gemm_fused", st)
+
+        def select():
+            st = L.fp8bq_topk_bf16(m, v, kk, logits.data_ptr(), work.data_ptr(), wsb, idx.data_ptr(),
+                                   val.data_ptr(), s)
+            if st:
+                raise fp8bq.Fp8bqError("fp8bq_topk_bf16", st)
+
+        def exact():
+            st = L.fp8bq_rescore_bf16(m, k, v, kk, h.data_ptr(), wbf.data_ptr(), idx.data_ptr(), scores.data_ptr(),
+                                      pick.data_ptr(), s)
+            if st:
+                raise fp8bq.Fp8bqError("fp8bq_rescore_bf16", st)
+
+        def pipeline():
+            coarse()
+            select()
+            exact()
+
+        def full_bf16():
+            torch.matmul(h, wbf.t())
+
+        row = {"M": m, "V": v, "K": k, "k": kk}
+        for name, fn in (("coarse_us", coarse), ("topk_us", select), ("rescore_us", exact),
+                         ("pipeline_us", pipeline), ("torch_bf16_full_us", full_bf16)):
+            fn()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            e1.synchronize()
+            row[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        row["coarse_GBps"] = round(bf16_act_bytes(m, v, k) / (row["coarse_us"] * 1e-6) / 1e9, 1)
+        # bytes the pipeline must move: the FP8 projection and its scales, the
+        # survivors' bf16 rows, the hidden state, the logits written and read
+        pipe_bytes = bf16_act_bytes(m, v, k) + 2 * m * v + 2 * m * kk * k
+        row["pipeline_GBps"] = round(pipe_bytes / (row["pipeline_us"] * 1e-6) / 1e9, 1)
+        row["bf16_full_bytes"] = 2 * v * k
+        out.append(row)
+        print(f"bench: two-stage M={m}: {row}", file=sys.stderr, flush=True)
+    return out
+
+
 SWEEP_M = [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 33, 48, 64, 65, 96, 128, 129, 192, 256, 384, 512, 1024,
            2048, 3465, 4096]
 
@@ -325,6 +407,7 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=96)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=3465 prefill GEMM timing")
+    ap.add_argument("--no-two-stage", action="store_true", help="skip the two-stage vocabulary scoring timing")
     ap.add_argument("--m-sweep", action="store_true",
                     help="instead of the benchmark, time fp8bq_gemm over an M grid on the five shapes (one JSON line)")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -471,6 +554,11 @@ def main():
     if not args.no_prefill:
         print("bench: timing the prefill GEMMs", file=sys.stderr, flush=True)
         rec["prefill"] = prefill(plan)
+    if not args.no_two_stage:
+        print("bench: timing two-stage vocabulary scoring", file=sys.stderr, flush=True)
+        del plan
+        torch.cuda.empty_cache()
+        rec["two_stage"] = two_stage()
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline()

@@ -202,8 +202,9 @@ int64_t fp8bq_topk_workspace_bytes(int64_t M, int64_t V, int64_t k);
  *   val_bf16_out [M, k] bf16, written: their logit bit patterns.
  * Bit-exact (an order, no arithmetic); deterministic.
  * M == 0 is a quick return. Errors: k < 1, k > 256 or k > V; V >= 2^31;
- * M*V > 2^40; more than 2^21 chunks of 4096 logits in all (M * ceil(V /
- * 4096)); workspace_bytes too small; NULL pointer; logits, workspace or
+ * M*V > 2^40; more than 2^21 first-level workgroups (M * ceil(ceil(V / 1024)
+ * / G), G = min(4, floor(1024 / k))); workspace_bytes too small; NULL
+ * pointer; logits, workspace or
  * val_bf16_out not 16-B aligned, idx_out not 4-B aligned; device not gfx950.
  */
 int fp8bq_topk_bf16(int64_t M, int64_t V, int64_t k, const void *logits_bf16, void *workspace,

@@ -11,23 +11,26 @@
 // Order: a bf16 value's 16-bit key is its bit pattern mapped to a monotone
 // unsigned order (negative patterns inverted, positive ones with the top bit
 // set, so -0 sits just below +0); entries compare by key, equal keys by the
-// lower index. Packed with the inverted index below the key, every entry of a
-// row is a distinct unsigned word, so selecting the largest words is exact
-// and deterministic, and the value 0 (below every packed entry) pads.
+// lower index.
 //
-// Top-k uses the bitonic top-k network (Shanbhag, Pirk, Madden, "Efficient
-// Top-K Query Processing on Massively Parallel Hardware", SIGMOD 2018): with
-// p the power of two >= k, sort segments of p with alternating directions,
-// then repeatedly keep the element-wise maximum of each (ascending,
-// descending) pair of segments -- the bitonic half-cleaner step, which holds
-// the top p of the pair -- and bitonic-merge it, until one segment of p
-// remains. Every step is a fixed compare-exchange pattern in LDS: no atomics,
-// no data-dependent control flow, and far fewer stages than a full sort.
-//   launch 1: a workgroup per 4096-logit chunk of a row writes the chunk's
-//             top k as 64-bit words (key << 32 | ~index) to the workspace;
-//   launch 2+: a workgroup per 4096 / p such lists merges them into one;
-//             repeated until each row has one list, written as indices and
-//             bf16 values.
+// Top-k, exact, with no atomics and no sort network: a wave holds up to 1024
+// candidates (16 per lane, position 64 r + lane in register r) and selects
+// its k best directly. It bisects the 16-bit key space for the k-th largest
+// key t, counting candidates with a ballot and a popcount per register (16
+// steps, no barriers); takes every candidate above t, and of those equal to t
+// the lowest positions, ranked by ballot prefix counts; and writes the k
+// chosen in position order. Candidate lists are kept in index order at every
+// level, so position order is index order and ties go to the lower index.
+//   launch 1: a workgroup of G waves per G chunks of 1024 logits; each wave
+//             selects its chunk's k best into LDS, then wave 0 selects the
+//             workgroup's k best from those G k candidates (G = min(4,
+//             1024 / k));
+//   launch 2+: a workgroup of up to min(16, 1024 / k) waves; each wave
+//             selects the k best of 1024 / k lists, then wave 0 the k best
+//             of the waves' results; repeated until a row has one list
+//             (one merge launch for up to 256 first-level lists at k = 64).
+// The last selection orders its k by (key descending, index ascending), each
+// entry counting the entries ranked above it, and writes indices and values.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,122 +41,194 @@ namespace fp8bq {
 
 namespace {
 
-constexpr int kChunk = 4096;          // logits per first-level workgroup
-constexpr int kChunkThreads = 1024;
-constexpr int kMergeEntries = 4096;   // 64-bit entries per merge workgroup (32 KiB LDS)
-constexpr int kMergeThreads = 512;
+constexpr int kPer = 16;                  // candidates per lane
+constexpr int kWaveCand = 64 * kPer;      // candidates per wave
+constexpr int kMaxGroup = 16;             // waves per workgroup (at most)
+constexpr int kChunkGroup = 4;            // chunk waves per first-level workgroup
 
 __device__ __forceinline__ unsigned key16(unsigned b) { return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u); }
 __device__ __forceinline__ unsigned unkey16(unsigned key) { return (key & 0x8000u) ? (key & 0x7fffu) : (~key & 0xffffu); }
 
-template <typename T>
-__device__ __forceinline__ void compare_exchange(T* a, int lo, int hi, bool up) {
-  const T x = a[lo], y = a[hi];
-  if ((x > y) == up) {
-    a[lo] = y;
-    a[hi] = x;
+__device__ __forceinline__ int lanes_below(unsigned long long mask) {
+  return static_cast<int>(
+      __builtin_amdgcn_mbcnt_hi(static_cast<unsigned>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0u)));
+}
+
+// Largest and smallest value over the wave: DPP within each row of 16 lanes
+// (swap neighbours, swap pairs, mirror halves, mirror the row), then the four
+// row results read as scalars.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp(unsigned v) {
+  return static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ unsigned umax(unsigned a, unsigned b) { return a > b ? a : b; }
+__device__ __forceinline__ unsigned umin(unsigned a, unsigned b) { return a < b ? a : b; }
+
+__device__ __forceinline__ void wave_max_min(unsigned v, unsigned* vmax, unsigned* vmin) {
+  unsigned hi = v, lo = v;
+  hi = umax(hi, dpp<0xB1>(hi));  // quad_perm [1, 0, 3, 2]
+  lo = umin(lo, dpp<0xB1>(lo));
+  hi = umax(hi, dpp<0x4E>(hi));  // quad_perm [2, 3, 0, 1]
+  lo = umin(lo, dpp<0x4E>(lo));
+  hi = umax(hi, dpp<0x141>(hi));  // row_half_mirror
+  lo = umin(lo, dpp<0x141>(lo));
+  hi = umax(hi, dpp<0x140>(hi));  // row_mirror
+  lo = umin(lo, dpp<0x140>(lo));
+  *vmax = umax(umax(__builtin_amdgcn_readlane(hi, 0), __builtin_amdgcn_readlane(hi, 16)),
+               umax(__builtin_amdgcn_readlane(hi, 32), __builtin_amdgcn_readlane(hi, 48)));
+  *vmin = umin(umin(__builtin_amdgcn_readlane(lo, 0), __builtin_amdgcn_readlane(lo, 16)),
+               umin(__builtin_amdgcn_readlane(lo, 32), __builtin_amdgcn_readlane(lo, 48)));
+}
+
+// Candidates: key[r] = 1 + the 16-bit key (0 = empty, never chosen), idx[r]
+// its vocabulary index, at position 64 r + lane. Writes the k best -- by key,
+// equal keys by lower position -- to dst[0 .. k) in position order, padded
+// with empty entries when fewer than k are not empty. One whole wave calls it.
+template <int PER>
+__device__ void wave_select(const unsigned (&key)[PER], const unsigned (&idx)[PER], int k, v2u* dst) {
+  const int lane = threadIdx.x & 63;
+  // t: the largest key with at least k candidates at or above it (1 when
+  // fewer than k candidates are not empty). It lies in [lo, hi): hi is one
+  // past the largest key; for k <= 64 every lane holds a key at or above the
+  // smallest lane maximum, so that is a valid lo.
+  unsigned lane_max = key[0];
+#pragma unroll
+  for (int r = 1; r < PER; ++r) lane_max = umax(lane_max, key[r]);
+  unsigned wmax, wmin;
+  wave_max_min(lane_max, &wmax, &wmin);
+  unsigned hi = wmax + 1u;
+  unsigned lo = (k <= 64 && wmin > 1u && wmin < hi) ? wmin : 1u;
+  for (int step = 0; step < 17 && hi - lo > 1u; ++step) {
+    const unsigned mid = (lo + hi) >> 1;
+    int count = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) count += __popcll(__ballot(key[r] >= mid));
+    if (count >= k) {
+      lo = mid;
+    } else {
+      hi = mid;
+    }
+  }
+  const unsigned t = lo;
+  int above = 0;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) above += __popcll(__ballot(key[r] > t));
+  const int need = k - above;  // candidates equal to t to take, lowest positions first
+  int ties_before = 0;
+  int out = 0;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const unsigned long long tie = __ballot(key[r] == t);
+    const bool take = key[r] > t || (key[r] == t && ties_before + lanes_below(tie) < need);
+    ties_before += __popcll(tie);
+    const unsigned long long taken = __ballot(take);
+    if (take) dst[out + lanes_below(taken)] = v2u{key[r], idx[r]};
+    out += __popcll(taken);
+  }
+  for (int j = out + lane; j < k; j += 64) dst[j] = v2u{0u, 0u};
+}
+
+// The k best of the n (<= 1024) candidates src[0 .. n) (position order),
+// written to dst as wave_select does. One whole wave calls it.
+template <int PER>
+__device__ void select_from(const v2u* src, int n, int k, v2u* dst) {
+  const int lane = threadIdx.x & 63;
+  unsigned key[PER], idx[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int p = 64 * r + lane;
+    const v2u e = p < n ? src[p] : v2u{0u, 0u};
+    key[r] = e[0];
+    idx[r] = e[1];
+  }
+  wave_select<PER>(key, idx, k, dst);
+}
+
+__device__ void select_list(const v2u* src, int n, int k, v2u* dst) {
+  if (n <= 256) {
+    select_from<4>(src, n, k, dst);
+  } else {
+    select_from<16>(src, n, k, dst);
   }
 }
 
-// Leaves the p largest of a[0 .. e) in a[0 .. p), in descending order.
-// e and p are powers of two with e >= 2 p; entries are distinct or padding.
-// The whole block calls it; it ends with a barrier.
-template <typename T>
-__device__ void bitonic_top(T* a, int e, int p, int log_p) {
-  const int tid = threadIdx.x;
-  const int nt = blockDim.x;
-  __syncthreads();
-  // sort every segment of p: even segments ascending, odd ones descending
-  for (int size = 2; size <= p; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < e / 2; i += nt) {
-        const int lo = 2 * i - (i & (stride - 1));
-        compare_exchange(a, lo, lo + stride, (lo & size) == 0);
-      }
-      __syncthreads();
+// sel[0 .. k): a row's k best in position order (all non-empty). Writes them
+// ordered by (key descending, position ascending): each entry's slot is the
+// number of entries ranked above it. One whole wave calls it.
+__device__ void wave_place(const v2u* sel, int k, int* __restrict__ out_idx, unsigned short* __restrict__ out_val) {
+  const int lane = threadIdx.x & 63;
+  for (int i = lane; i < k; i += 64) {
+    const v2u e = sel[i];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < k; ++j) {
+      const v2u f = sel[j];
+      rank += (f[0] > e[0]) | ((f[0] == e[0]) & (j < i));
     }
-  }
-  // halve: segments sit gap apart; the pair (2j, 2j + 1) becomes segment j
-  // at offset 2 j gap, merged ascending for even j and descending for odd j
-  // (descending on the last level)
-  for (int gap = p; gap < e; gap <<= 1) {
-    const int pairs = e / (2 * gap);
-    for (int i = tid; i < pairs * p; i += nt) {
-      const int lo = 2 * (i >> log_p) * gap + (i & (p - 1));
-      const T x = a[lo], y = a[lo + gap];
-      a[lo] = x > y ? x : y;
-    }
-    __syncthreads();
-    const int half = p >> 1;
-    for (int stride = half; stride > 0; stride >>= 1) {
-      for (int i = tid; i < pairs * half; i += nt) {
-        const int j = i >> (log_p - 1);
-        const int t = i & (half - 1);
-        const int lo = 2 * j * gap + 2 * t - (t & (stride - 1));
-        compare_exchange(a, lo, lo + stride, pairs > 1 && (j & 1) == 0);
-      }
-      __syncthreads();
-    }
+    out_idx[rank] = static_cast<int>(e[1]);
+    out_val[rank] = static_cast<unsigned short>(unkey16(e[0] - 1u));
   }
 }
 
-__global__ __launch_bounds__(kChunkThreads) void topk_chunk_kernel(int64_t v, int k, int p, int log_p, int chunks,
-                                                                   const unsigned short* __restrict__ logits,
-                                                                   unsigned long long* __restrict__ lists) {
-  __shared__ unsigned buf[kChunk];
-  const int64_t row = blockIdx.x / chunks;
-  const int chunk = static_cast<int>(blockIdx.x - row * chunks);
-  const int64_t base = static_cast<int64_t>(chunk) * kChunk;
+__global__ __launch_bounds__(64 * kMaxGroup) void topk_chunk_kernel(int64_t v, int k, int group, int parts,
+                                                                    const unsigned short* __restrict__ logits,
+                                                                    v2u* __restrict__ lists,
+                                                                    int* __restrict__ out_idx,
+                                                                    unsigned short* __restrict__ out_val) {
+  __shared__ v2u wave_lists[kWaveCand];  // group * k <= 1024
+  __shared__ v2u best[256];
+  const int64_t row = blockIdx.x / parts;
+  const int part = static_cast<int>(blockIdx.x - row * parts);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t base = (static_cast<int64_t>(part) * group + wave) * kWaveCand;
   const unsigned short* x = logits + row * v;
-  for (int i = threadIdx.x; i < kChunk; i += kChunkThreads) {
-    const int64_t gi = base + i;
-    buf[i] = gi < v ? (key16(x[gi]) << 16) | (0xffffu - static_cast<unsigned>(i)) : 0u;
+  unsigned key[kPer], idx[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t pos = base + 64 * r + lane;
+    key[r] = pos < v ? key16(x[pos]) + 1u : 0u;
+    idx[r] = static_cast<unsigned>(pos);
   }
-  bitonic_top(buf, kChunk, p, log_p);
-  unsigned long long* out = lists + (row * chunks + chunk) * k;
-  for (int j = threadIdx.x; j < k; j += kChunkThreads) {
-    const unsigned w = buf[j];
-    const unsigned gi = static_cast<unsigned>(base) + (0xffffu - (w & 0xffffu));
-    out[j] = w == 0u ? 0ull : (static_cast<unsigned long long>(w >> 16) << 32) | (0xffffffffu - gi);
+  wave_select<kPer>(key, idx, k, wave_lists + wave * k);
+  __syncthreads();
+  if (wave != 0) return;
+  if (parts > 1) {
+    select_list(wave_lists, group * k, k, lists + (row * parts + part) * k);
+  } else {
+    select_list(wave_lists, group * k, k, best);
+    __builtin_amdgcn_wave_barrier();
+    wave_place(best, k, out_idx + row * k, out_val + row * k);
   }
 }
 
-// Merges `lists` sorted lists of k per row, `fan` lists per workgroup.
-// Writes `lists_out` = ceil(lists / fan) lists per row to `next`, or, when
-// that is 1, the row's final indices and values.
-__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(int k, int p, int log_p, int lists, int fan,
-                                                                   const unsigned long long* __restrict__ src,
-                                                                   unsigned long long* __restrict__ next,
-                                                                   int* __restrict__ out_idx,
-                                                                   unsigned short* __restrict__ out_val) {
-  __shared__ unsigned long long buf[kMergeEntries];
-  const int lists_out = (lists + fan - 1) / fan;
+// Merges `lists` lists of k per row: wave w of a workgroup selects the k
+// best of `fan` consecutive lists, then wave 0 selects the k best of the
+// waves' results, so a workgroup turns `fan` * (its waves) lists into one
+// list of `next`, or, on the last level, into the row's ordered output.
+__global__ __launch_bounds__(64 * kMaxGroup) void topk_merge_kernel(int k, int lists, int fan,
+                                                                    const v2u* __restrict__ src,
+                                                                    v2u* __restrict__ next, int* __restrict__ out_idx,
+                                                                    unsigned short* __restrict__ out_val) {
+  __shared__ v2u wave_lists[kWaveCand];  // waves * k <= 1024
+  __shared__ v2u best[256];
+  const int waves = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6;
+  const int span = fan * waves;
+  const int lists_out = (lists + span - 1) / span;
   const int64_t row = blockIdx.x / lists_out;
   const int part = static_cast<int>(blockIdx.x - row * lists_out);
-  const int first = part * fan;
-  const int count = lists - first < fan ? lists - first : fan;
-  int segs = 2;
-  while (segs < count) segs <<= 1;
-  const int e = segs * p;
-  const unsigned long long* in = src + (row * lists + first) * k;
-  // list f lands in segment f: reversed (ascending) for even f, as is
-  // (descending) for odd f, padded with 0 to p entries
-  for (int i = threadIdx.x; i < e; i += kMergeThreads) {
-    const int f = i >> log_p;
-    const int s = i & (p - 1);
-    const int j = (f & 1) ? s : p - 1 - s;
-    buf[i] = (f < count && j < k) ? in[static_cast<int64_t>(f) * k + j] : 0ull;
-  }
-  bitonic_top(buf, e, p, log_p);
+  const int first = part * span + wave * fan;
+  const int count = lists - first < fan ? lists - first : fan;  // may be <= 0: no candidates
+  select_list(src + (row * lists + first) * k, count > 0 ? count * k : 0, k, wave_lists + wave * k);
+  __syncthreads();
+  if (wave != 0) return;
   if (lists_out > 1) {
-    unsigned long long* out = next + (row * lists_out + part) * k;
-    for (int j = threadIdx.x; j < k; j += kMergeThreads) out[j] = buf[j];
+    select_list(wave_lists, waves * k, k, next + (row * lists_out + part) * k);
   } else {
-    for (int j = threadIdx.x; j < k; j += kMergeThreads) {
-      const unsigned long long w = buf[j];
-      out_idx[row * k + j] = static_cast<int>(0xffffffffu - static_cast<unsigned>(w));
-      out_val[row * k + j] = static_cast<unsigned short>(unkey16(static_cast<unsigned>(w >> 32)));
-    }
+    select_list(wave_lists, waves * k, k, best);
+    __builtin_amdgcn_wave_barrier();
+    wave_place(best, k, out_idx + row * k, out_val + row * k);
   }
 }
 
@@ -230,44 +305,50 @@ __global__ __launch_bounds__(64) void pick_kernel(int k, const int* __restrict__
   if (threadIdx.x == 0) pick[row] = bi;
 }
 
-int pow2_at_least(int x) {
-  int p = 1;
-  while (p < x) p <<= 1;
-  return p;
+int topk_group(int64_t k) { return static_cast<int>(kChunkGroup < kWaveCand / k ? kChunkGroup : kWaveCand / k); }
+
+// Waves of a merge workgroup: each takes kWaveCand / k lists; the workgroup
+// holds no more waves than its lists need, nor more than wave 0 can merge.
+int merge_waves(int lists, int k) {
+  const int fan = kWaveCand / k;
+  const int cap = kMaxGroup < kWaveCand / k ? kMaxGroup : kWaveCand / k;
+  const int need = (lists + fan - 1) / fan;
+  return need < cap ? need : cap;
 }
 
-int log2_exact(int p) { return __builtin_ctz(static_cast<unsigned>(p)); }
-
-int64_t chunks_of(int64_t v) { return (v + kChunk - 1) / kChunk; }
+int64_t topk_parts(int64_t v, int64_t k) {
+  const int64_t chunks = (v + kWaveCand - 1) / kWaveCand;
+  return (chunks + topk_group(k) - 1) / topk_group(k);
+}
 
 }  // namespace
 
 int64_t topk_workspace_bytes(int64_t m, int64_t v, int64_t k) {
-  const int64_t fan = kMergeEntries / pow2_at_least(static_cast<int>(k));
-  const int64_t l0 = chunks_of(v);
-  const int64_t l1 = (l0 + fan - 1) / fan;
-  return (l0 + l1) * m * k * static_cast<int64_t>(sizeof(unsigned long long));
+  const int64_t l1 = topk_parts(v, k);
+  const int64_t fan = kWaveCand / k;
+  const int64_t l2 = (l1 + fan - 1) / fan;
+  return (l1 + l2) * m * k * static_cast<int64_t>(sizeof(v2u));
 }
 
-int64_t topk_grid_blocks(int64_t m, int64_t v) { return m * chunks_of(v); }
+int64_t topk_grid_blocks(int64_t m, int64_t v, int64_t k) { return m * topk_parts(v, k); }
 
 hipError_t launch_topk(int64_t m, int64_t v, int k, const void* logits, void* workspace, int* idx, void* val,
                        hipStream_t stream) {
-  const int p = pow2_at_least(k);
-  const int log_p = log2_exact(p);
-  const int fan = kMergeEntries / p;
-  int lists = static_cast<int>(chunks_of(v));
-  auto* a = static_cast<unsigned long long*>(workspace);
-  auto* b = a + static_cast<int64_t>(lists) * m * k;  // the second level's lists
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3(static_cast<unsigned>(m * lists)), dim3(kChunkThreads), 0, stream, v, k,
-                     p, log_p, lists, static_cast<const unsigned short*>(logits), a);
+  const int group = topk_group(k);
+  const int fan = kWaveCand / k;
+  int lists = static_cast<int>(topk_parts(v, k));
+  auto* a = static_cast<v2u*>(workspace);
+  auto* b = a + static_cast<int64_t>(lists) * m * k;  // the next level's lists
+  auto* out_val = static_cast<unsigned short*>(val);
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3(static_cast<unsigned>(m * lists)), dim3(64 * group), 0, stream, v, k,
+                     group, lists, static_cast<const unsigned short*>(logits), a, idx, out_val);
   hipError_t e = hipGetLastError();
-  while (e == hipSuccess) {
-    const int lists_out = (lists + fan - 1) / fan;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<unsigned>(m * lists_out)), dim3(kMergeThreads), 0, stream, k,
-                       p, log_p, lists, fan, a, b, idx, static_cast<unsigned short*>(val));
+  while (e == hipSuccess && lists > 1) {
+    const int waves = merge_waves(lists, k);
+    const int lists_out = (lists + fan * waves - 1) / (fan * waves);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(static_cast<unsigned>(m * lists_out)), dim3(64 * waves), 0, stream, k,
+                       lists, fan, a, b, idx, out_val);
     e = hipGetLastError();
-    if (lists_out == 1) break;
     lists = lists_out;
     auto* t = a;
     a = b;

@@ -133,13 +133,14 @@ def test_fused_errors(fp8bq):
 
 def test_topk_workspace_size(fp8bq):
     L = fp8bq.lib()
-    # first level: one list of k per 4096 logits; second: one per 4096 / p lists
-    # (p = power of two >= k), 8 bytes an entry
-    for m, v, k in ((1, 152064, 64), (4, 152064, 50), (3, 4096, 256), (2, 4097, 1), (1, 10, 10), (16, 1 << 20, 7)):
-        p = 1 << (k - 1).bit_length()
-        l0 = -(-v // 4096)
-        l1 = -(-l0 // (4096 // p))
-        assert L.fp8bq_topk_workspace_bytes(m, v, k) == (l0 + l1) * m * k * 8, (m, v, k)
+    # first level: one list of k per G chunks of 1024 logits (G = min(4,
+    # 1024 // k)); second: at most one per 1024 // k lists; 8 bytes an entry
+    for m, v, k in ((1, 152064, 64), (4, 152064, 50), (3, 4096, 256), (2, 4097, 1), (1, 10, 10), (16, 1 << 20, 7),
+                    (2, 300000, 100)):
+        g = min(4, 1024 // k)
+        l1 = -(-(-(-v // 1024)) // g)
+        l2 = -(-l1 // (1024 // k))
+        assert L.fp8bq_topk_workspace_bytes(m, v, k) == (l1 + l2) * m * k * 8, (m, v, k)
     assert L.fp8bq_topk_workspace_bytes(0, 100, 5) == 8 * 0
     assert L.fp8bq_topk_workspace_bytes(1, 100, 0) == -2
     assert L.fp8bq_topk_workspace_bytes(1, 100, 257) == -2
@@ -157,7 +158,7 @@ def test_topk_errors(fp8bq):
     assert L.fp8bq_topk_bf16(2, 7, 8, p, p, ws, p, p, None) == -2  # k > V
     assert L.fp8bq_topk_bf16(-1, 1000, 8, p, p, ws, p, p, None) == -2
     assert L.fp8bq_topk_bf16(2, 1 << 31, 8, p, p, ws, p, p, None) == -2
-    assert L.fp8bq_topk_bf16(1 << 12, 1 << 22, 8, p, p, 1 << 40, p, p, None) == -2  # 2^22 chunks
+    assert L.fp8bq_topk_bf16(1 << 11, 1 << 24, 8, p, p, 1 << 40, p, p, None) == -2  # 2^22 workgroups
     assert L.fp8bq_topk_bf16(2, 1000, 8, p, p, ws - 1, p, p, None) == -2
     assert L.fp8bq_topk_bf16(0, 1000, 8, None, None, 0, None, None, None) == 0
     assert L.fp8bq_topk_bf16(2, 1000, 8, None, p, ws, p, p, None) == -1
