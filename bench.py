@@ -408,6 +408,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=3465 prefill GEMM timing")
     ap.add_argument("--no-two-stage", action="store_true", help="skip the two-stage vocabulary scoring timing")
+    ap.add_argument("--only", choices=("prefill", "two-stage"),
+                    help="run only this leg and print its JSON line (for profiling one kernel family)")
     ap.add_argument("--m-sweep", action="store_true",
                     help="instead of the benchmark, time fp8bq_gemm over an M grid on the five shapes (one JSON line)")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -423,6 +425,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+
+    if args.only == "two-stage":
+        print(json.dumps({"metric": "two-stage vocabulary scoring us/call", "data": "synthetic",
+                          "two_stage": two_stage(), "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
+    if args.only == "prefill":
+        print(json.dumps({"metric": "prefill block-FP8 GEMM us/call", "data": "synthetic",
+                          "prefill": prefill(Plan(1)), "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
 
     if args.m_sweep:
         print(json.dumps({"metric": "fp8bq_gemm us/call over M", "data": "synthetic", "rows": m_sweep(),
