@@ -73,7 +73,7 @@ def kernel_source_digest():
     to the code it was taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "memory_bound_w8a8_amd", "csrc")
-    for f in ("device_common.h", "gemm_rows.h", "gemm.hip"):
+    for f in ("device_common.h", "gemm_rows.h", "rows_launch.h", "gemm_fused.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -540,8 +540,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "gemm_rows_kernel<16, 8, 5, 5, 6, 2> (fused quantisation + GEMM, the M=1..8 launches; HIP "
-                      "events on the launch stream around back-to-back launches)",
+            "kernel": "gemm_rows_kernel<16, 8, 5, 5, 6, 2, TOK> (fused quantisation + GEMM; TOK = 1, 2, 4, 8 for "
+                      "M = 1, 2, 3..4, 5..8; the M=1..8 launches, HIP events on the launch stream around "
+                      "back-to-back launches)",
         },
         "unfused": {
             "path": "fp8bq_quant_act then fp8bq_gemm per M (two launches), same weights and activations",

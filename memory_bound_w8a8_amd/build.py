@@ -32,6 +32,10 @@ HIPCC_FLAGS = [
     # MFMA results in ordinary VGPRs: the per-group scale FMAs read them
     # directly instead of copying each out of an accumulation register
     "-mllvm", "-amdgpu-mfma-vgpr-form=true",
+    # unroll the chunk loops in full even where in-kernel quantisation makes
+    # them long: a partly rolled loop indexes the register arrays at run time,
+    # which puts them in scratch memory
+    "-mllvm", "-pragma-unroll-threshold=1000000",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -168,7 +168,7 @@ int64_t fp8bq_topk_workspace_bytes(int64_t M, int64_t V, int64_t k) {
 int fp8bq_topk_bf16(int64_t M, int64_t V, int64_t k, const void* logits_bf16, void* workspace,
                     int64_t workspace_bytes, int32_t* idx_out, void* val_bf16_out, void* stream) {
   if (M < 0 || V < 0 || V > kMaxIndex || k < 1 || k > kTopkMaxK || k > V || !product_ok(M, V)) return FP8BQ_ERR_SHAPE;
-  if (fp8bq::topk_grid_blocks(M, V) > kMaxGridBlocks) return FP8BQ_ERR_SHAPE;
+  if (fp8bq::topk_grid_blocks(M, V, k) > kMaxGridBlocks) return FP8BQ_ERR_SHAPE;
   if (M == 0) return FP8BQ_OK;
   if (workspace_bytes < fp8bq::topk_workspace_bytes(M, V, k)) return FP8BQ_ERR_SHAPE;
   if (logits_bf16 == nullptr || workspace == nullptr || idx_out == nullptr || val_bf16_out == nullptr)

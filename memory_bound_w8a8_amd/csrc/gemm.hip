@@ -20,41 +20,11 @@
 #include "gemm_tiled.h"
 #include "gemm_w8a16.h"
 #include "launch.h"
+#include "rows_launch.h"
 
 namespace fp8bq {
 
 namespace {
-
-constexpr int kNumCUs = 256;   // MI355X
-constexpr int kRowsWaves = 8;  // waves per workgroup in the row-range kernel
-constexpr int kMaxTiles = 5;
-constexpr int kMaxGroupsPerWave = 9;
-
-struct GemmArgs {
-  int64_t m, n, k;
-  const void* aq;
-  const float* as;
-  const void* wq;
-  const float* ws;
-  void* c;
-  hipStream_t stream;
-};
-
-using Launch = hipError_t (*)(const GemmArgs&, int64_t rows_per_wg);
-
-template <int MT, int AF, int TILES, int GMAX>
-hipError_t rows_instance(const GemmArgs& a, int64_t rows_per_wg) {
-  // chunks of weight loads kept in flight per wave (fewer where the held
-  // activation of a 32-token tile, or the bf16 activation awaiting
-  // quantisation, already takes most registers)
-  constexpr int PD = AF == kActBf16 ? (GMAX >= 8 ? 2 : (GMAX >= 7 ? 4 : 6)) : (MT == 16 ? 6 : 4);
-  const unsigned grid = static_cast<unsigned>((a.n + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((gemm_rows_kernel<MT, kRowsWaves, GMAX, TILES, PD, AF>), dim3(grid), dim3(64 * kRowsWaves), 0,
-                     a.stream, static_cast<int>(a.m), a.n, a.k, rows_per_wg,
-                     static_cast<const unsigned char*>(a.aq), a.as, static_cast<const unsigned char*>(a.wq), a.ws,
-                     static_cast<unsigned short*>(a.c));
-  return hipGetLastError();
-}
 
 template <int TILES, int GMAX>
 hipError_t rows64_instance(const GemmArgs& a, int64_t rows_per_wg) {
@@ -79,8 +49,6 @@ constexpr Launch rows_entry() {
     return &rows64_instance<TILES, GMAX>;
   else if constexpr (TT == 8)
     return &rows_instance<16, kActCodes, TILES, GMAX>;
-  else if constexpr (TT == 0)  // bf16 activation quantised in the kernel, up to 16 tokens
-    return &rows_instance<16, kActBf16, TILES, GMAX>;
   else
     return &rows_instance<TT, kActCodeLines, TILES, GMAX>;
 }
@@ -120,7 +88,6 @@ constexpr std::array<std::array<Launch, kMaxGroupsPerWave>, sizeof...(T)> w8a16_
 constexpr auto kW8A16 = w8a16_table(std::make_integer_sequence<int, kMaxTiles>{});
 
 constexpr auto kRows8 = rows_table<8>(std::make_integer_sequence<int, kMaxTiles>{});
-constexpr auto kRowsFused = rows_table<0>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows16 = rows_table<16>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows32 = rows_table<32>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows64 = rows_table<64>(std::make_integer_sequence<int, kMaxTiles>{});
@@ -175,15 +142,6 @@ bool small_m_supported(int64_t m, int64_t n, int64_t k) {
   int64_t rows_per_wg;
   int tiles, gmax;
   return m >= 1 && m <= 16 && rows_shape(n, k, &rows_per_wg, &tiles, &gmax);
-}
-
-hipError_t launch_gemm_fused(int64_t m, int64_t n, int64_t k, const void* a, const void* wq, const float* ws, void* c,
-                             hipStream_t stream) {
-  const GemmArgs args{m, n, k, a, nullptr, wq, ws, c, stream};
-  int64_t rows_per_wg;
-  int tiles, gmax;
-  if (m < 1 || m > 16 || !rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) return hipErrorInvalidValue;
-  return kRowsFused[tiles - 1][gmax - 1](args, rows_per_wg);
 }
 
 hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, const void* wq, const float* ws, void* c,

@@ -67,7 +67,16 @@ enum ActForm : int {
 // r == 0 else fma(r, y, q0). An exhaustive GPU check over every bf16 x and
 // every bf16 amax >= |x| found the e4m3 codes of this quotient equal to
 // those of the IEEE division whenever amax >= 2^-104; below 2^-96 the IEEE
-// division is used instead.
+// division is used instead. fma(r, y, q0) equals q0 when r == 0 and x != 0
+// (adding a zero to a non-zero value is exact) and has the sign of x
+// otherwise, so the select is written as copysign(fma(r, y, q0), x), which
+// differs only for x = -0, where it keeps the sign as the select did.
+__device__ __forceinline__ float quotient_e4m3_range(float x, float s, float y) {
+  const float q0 = x * y;
+  const float r = fmaf(-q0, s, x);
+  return fminf(fmaxf(copysignf(fmaf(r, y, q0), x), -kE4m3Max), kE4m3Max);
+}
+
 __device__ __forceinline__ v8i quant_group_operand(const v4u (&raw)[4], float* scale) {
   float x[32];
 #pragma unroll
@@ -88,18 +97,10 @@ __device__ __forceinline__ v8i quant_group_operand(const v4u (&raw)[4], float* s
   if (amax >= 0x1p-96f) {
     const float y = 1.0f / s;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      float q[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float xv = x[4 * d + e];
-        const float q0 = xv * y;
-        const float r = fmaf(-q0, s, xv);
-        const float qq = r == 0.f ? q0 : fmaf(r, y, q0);
-        q[e] = fminf(fmaxf(qq, -kE4m3Max), kE4m3Max);
-      }
-      out[d] = static_cast<int>(encode4_e4m3(q[0], q[1], q[2], q[3]));
-    }
+    for (int d = 0; d < 8; ++d)
+      out[d] = static_cast<int>(encode4_e4m3(quotient_e4m3_range(x[4 * d], s, y), quotient_e4m3_range(x[4 * d + 1], s, y),
+                                             quotient_e4m3_range(x[4 * d + 2], s, y),
+                                             quotient_e4m3_range(x[4 * d + 3], s, y)));
   } else {
 #pragma unroll
     for (int d = 0; d < 8; ++d)
@@ -109,25 +110,119 @@ __device__ __forceinline__ v8i quant_group_operand(const v4u (&raw)[4], float* s
   return out;
 }
 
-template <int MT, int S, int GMAX, int TILES, int PD, int AF>
+// Largest value of v over each aligned group of LPT lanes (a power of two,
+// 1..64), returned to every lane of the group; v are bit patterns of
+// non-negative floats, whose order as unsigned integers is their order as
+// floats. DPP inside 16-lane rows (swap neighbours, swap pairs, mirror
+// half-rows, mirror rows), then the four row results read as scalars.
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_row(unsigned v) {
+  return static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ unsigned umax_u32(unsigned a, unsigned b) { return a > b ? a : b; }
+
+template <int LPT>
+__device__ __forceinline__ unsigned lane_group_umax(unsigned v) {
+  if constexpr (LPT >= 2) v = umax_u32(v, dpp_row<0xB1>(v));
+  if constexpr (LPT >= 4) v = umax_u32(v, dpp_row<0x4E>(v));
+  if constexpr (LPT >= 8) v = umax_u32(v, dpp_row<0x141>(v));
+  if constexpr (LPT >= 16) v = umax_u32(v, dpp_row<0x140>(v));
+  if constexpr (LPT >= 32) {
+    const unsigned r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const unsigned r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    if constexpr (LPT == 32)
+      v = (threadIdx.x & 32) ? umax_u32(r2, r3) : umax_u32(r0, r1);
+    else
+      v = umax_u32(umax_u32(r0, r1), umax_u32(r2, r3));
+  }
+  return v;
+}
+
+// Quantise one group for at most TOK (< 16) tokens with the values spread
+// over the wave instead of over the MFMA operand (where each lane would
+// quantise 32 values, mostly copies of other lanes'): lane l holds bf16
+// values V (l % LPT) .. V (l % LPT) + V - 1 of token l / LPT (LPT = 64 / TOK
+// lanes per token, V = 2 TOK, raw[] as bf16 pairs). Same rule as
+// quant_group_operand. The codes go to the wave's LDS slot (row = token,
+// 16-byte piece c of a row at 8 row + (c ^ (row & 7))), and the lane gets
+// back its MFMA operand, token min(l % 16, m_rows - 1), and that token's
+// scale. Requires m_rows <= TOK.
+template <int TOK>
+__device__ __forceinline__ v8i quant_group_compact(const v4u (&raw)[2], int m_rows, v4u* slot, float* scale) {
+  static_assert(TOK == 1 || TOK == 2 || TOK == 4 || TOK == 8, "TOK");
+  constexpr int LPT = 64 / TOK;
+  constexpr int V = 2 * TOK;
+  const int lane = threadIdx.x & 63;
+  const int tok = lane / LPT;
+  const int off = (lane % LPT) * V;  // first value (= code byte) of the lane in the token's group
+  float x[V];
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    x[2 * i] = bf16_lo(raw[i / 4][i % 4]);
+    x[2 * i + 1] = bf16_hi(raw[i / 4][i % 4]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < V; ++j) amax = fmaxf(amax, fabsf(x[j]));
+  amax = __builtin_bit_cast(float, lane_group_umax<LPT>(__builtin_bit_cast(unsigned, amax)));
+  const float s = group_scale(amax);
+  float q[V];
+  if (amax >= 0x1p-96f) {
+    const float y = 1.0f / s;
+#pragma unroll
+    for (int j = 0; j < V; ++j) q[j] = quotient_e4m3_range(x[j], s, y);
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) q[j] = scaled_clamped(x[j], s);
+  }
+  unsigned char* base = reinterpret_cast<unsigned char*>(slot);
+  unsigned char* dst = base + (8 * tok + ((off >> 4) ^ (tok & 7))) * 16 + (off & 15);
+  if constexpr (V == 2) {
+    *reinterpret_cast<unsigned short*>(dst) =
+        static_cast<unsigned short>(__builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false));
+  } else if constexpr (V == 4) {
+    *reinterpret_cast<unsigned*>(dst) = encode4_e4m3(q[0], q[1], q[2], q[3]);
+  } else if constexpr (V == 8) {
+    *reinterpret_cast<v2u*>(dst) = v2u{encode4_e4m3(q[0], q[1], q[2], q[3]), encode4_e4m3(q[4], q[5], q[6], q[7])};
+  } else {
+    *reinterpret_cast<v4u*>(dst) = v4u{encode4_e4m3(q[0], q[1], q[2], q[3]), encode4_e4m3(q[4], q[5], q[6], q[7]),
+                                       encode4_e4m3(q[8], q[9], q[10], q[11]),
+                                       encode4_e4m3(q[12], q[13], q[14], q[15])};
+  }
+  __builtin_amdgcn_wave_barrier();
+  const int lrow = lane & 15;
+  const int quarter = lane >> 4;
+  const int tm = lrow < m_rows ? lrow : m_rows - 1;
+  const v4u lo = slot[8 * tm + (quarter ^ (tm & 7))];
+  const v4u hi = slot[8 * tm + ((quarter + 4) ^ (tm & 7))];
+  __builtin_amdgcn_wave_barrier();
+  *scale = __shfl(s, tm * LPT);
+  return join8(lo, hi);
+}
+
+template <int MT, int S, int GMAX, int TILES, int PD, int AF, int TOK = 16>
 struct RowsKernel {
   static constexpr int kMS = MT / 16;        // 16-token tiles
   static constexpr int kChunks = TILES * GMAX;
   static constexpr int kRing = PD + 1;       // chunk register buffers
   static constexpr int kStageSlots = 2;      // LDS transpose slots per wave
-  static constexpr int kLdsBytes = S * kStageSlots * 2048 + S * TILES * kMS * 1024;
+  static constexpr int kLdsBytes =
+      S * kStageSlots * 2048 + S * TILES * kMS * 1024 + (AF == kActBf16 && TOK < 16 ? S * 2048 : 0);
 };
 
-template <int MT, int S, int GMAX, int TILES, int PD, int AF>
+template <int MT, int S, int GMAX, int TILES, int PD, int AF, int TOK = 16>
 __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n, int64_t k, int64_t rows_per_wg,
                                                            const unsigned char* __restrict__ aq,
                                                            const float* __restrict__ as,
                                                            const unsigned char* __restrict__ wq,
                                                            const float* __restrict__ ws,
                                                            unsigned short* __restrict__ c) {
-  using KC = RowsKernel<MT, S, GMAX, TILES, PD, AF>;
+  using KC = RowsKernel<MT, S, GMAX, TILES, PD, AF, TOK>;
   constexpr bool LINES = AF == kActCodeLines;
   constexpr bool BF16 = AF == kActBf16;
+  // bf16 activation of at most TOK < 16 tokens: quantised in the wave-wide
+  // layout of quant_group_compact (m_rows <= TOK)
+  constexpr bool COMPACT = BF16 && TOK < 16;
   static_assert(!BF16 || MT == 16, "in-kernel quantisation serves one 16-token tile");
   // Chunk order. Tile-major (all groups of tile 0, then tile 1, ...) keeps
   // one accumulator set; with in-kernel quantisation the order is
@@ -182,9 +277,15 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
   // (kActBf16: loaded with the group's first weight chunk, PD chunks ahead
   // of its first use, in load_chunk below; group-major order uses a group
   // for TILES consecutive chunks, so only a few groups are ever live.)
-  v4u araw[BF16 ? GMAX : 1][4];
+  v4u araw[BF16 ? GMAX : 1][COMPACT ? 2 : 4];
+  __shared__ v4u astage[COMPACT ? S : 1][128];
   const unsigned short* arow = nullptr;
-  if constexpr (BF16) {
+  if constexpr (COMPACT) {
+    constexpr int LPT = 64 / TOK;
+    int tok = lane / LPT;
+    tok = tok < m_rows ? tok : m_rows - 1;
+    arow = reinterpret_cast<const unsigned short*>(aq) + static_cast<int64_t>(tok) * k + (lane % LPT) * (2 * TOK);
+  } else if constexpr (BF16) {
     const int tok = lrow < m_rows ? lrow : m_rows - 1;
     arow = reinterpret_cast<const unsigned short*>(aq) + static_cast<int64_t>(tok) * k + 16 * quarter;
   } else {
@@ -231,10 +332,23 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     const int g = u < gcnt ? gbeg + u : glast;
     if (BF16 && t == 0) {
       const unsigned short* p = arow + static_cast<int64_t>(g) * kGroup;
-      araw[u][0] = *reinterpret_cast<const v4u*>(p);
-      araw[u][1] = *reinterpret_cast<const v4u*>(p + 8);
-      araw[u][2] = *reinterpret_cast<const v4u*>(p + 64);
-      araw[u][3] = *reinterpret_cast<const v4u*>(p + 72);
+      if constexpr (COMPACT) {  // 2 TOK bf16 values of one token
+        if constexpr (TOK == 1) {
+          araw[u][0][0] = *reinterpret_cast<const unsigned*>(p);
+        } else if constexpr (TOK == 2) {
+          const v2u d = *reinterpret_cast<const v2u*>(p);
+          araw[u][0][0] = d[0];
+          araw[u][0][1] = d[1];
+        } else {
+          araw[u][0] = *reinterpret_cast<const v4u*>(p);
+          if constexpr (TOK == 8) araw[u][1] = *reinterpret_cast<const v4u*>(p + 8);
+        }
+      } else {
+        araw[u][0] = *reinterpret_cast<const v4u*>(p);
+        araw[u][1] = *reinterpret_cast<const v4u*>(p + 8);
+        araw[u][2] = *reinterpret_cast<const v4u*>(p + 64);
+        araw[u][3] = *reinterpret_cast<const v4u*>(p + 72);
+      }
     }
     const int64_t off = static_cast<int64_t>(g) * kGroup + piece * 16;
     int64_t row0 = r_begin + 16 * t + lr8;
@@ -278,6 +392,11 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     const int t = GROUP_MAJOR ? ci % TILES : ci / GMAX;
     const int u = GROUP_MAJOR ? ci / TILES : ci % GMAX;
     v4f (&at)[MS] = acc[GROUP_MAJOR ? t : 0];
+    // With many groups per wave and in-kernel quantisation, keep the
+    // scheduler from hoisting later chunks' loads (and the activation
+    // values they bring) above this one: their registers would outgrow the
+    // budget and spill.
+    if constexpr (BF16 && GMAX >= 7) __builtin_amdgcn_sched_barrier(0);
     if (ci + PD < CH) load_chunk(ci + PD, (ci + PD) % RING);
     if (!GROUP_MAJOR && u == 0) {
 #pragma unroll
@@ -285,7 +404,10 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     }
     if (BF16 && t == 0) {  // first use of group u: quantise its activation
       float scale;
-      bv[u][0] = quant_group_operand(araw[u], &scale);
+      if constexpr (COMPACT)
+        bv[u][0] = quant_group_compact<TOK>(araw[u], m_rows, astage[wave], &scale);
+      else
+        bv[u][0] = quant_group_operand(araw[u], &scale);
       sa[u][0] = u < gcnt ? scale : 0.f;  // a group past the range adds nothing
     }
     if (LINES && t == 0) {  // first use of group u: its activation lines -> operand

@@ -34,7 +34,7 @@ hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, con
 // the workspace holds topk_workspace_bytes(m, v, k) bytes; the grids hold
 // topk_grid_blocks / rescore_grid_blocks workgroups of 1024 threads.
 int64_t topk_workspace_bytes(int64_t m, int64_t v, int64_t k);
-int64_t topk_grid_blocks(int64_t m, int64_t v);
+int64_t topk_grid_blocks(int64_t m, int64_t v, int64_t k);
 int64_t rescore_grid_blocks(int64_t m, int64_t k);
 hipError_t launch_topk(int64_t m, int64_t v, int k, const void* logits, void* workspace, int* idx, void* val,
                        hipStream_t stream);
