@@ -107,22 +107,6 @@ __global__ void fill_zero_kernel(unsigned short* __restrict__ c, int64_t count) 
 
 }  // namespace
 
-// Row-range launch shape for (N, K): rows per workgroup, tiles, groups
-// per wave. Returns false when the shape is outside the compiled table.
-bool rows_shape(int64_t n, int64_t k, int64_t* rows_per_wg, int* tiles, int* gmax) {
-  const int64_t groups = k / kGroup;
-  const int64_t g = (groups + kRowsWaves - 1) / kRowsWaves;
-  if (g < 1 || g > kMaxGroupsPerWave) return false;
-  int64_t r = (n + kNumCUs - 1) / kNumCUs;
-  r = (r + 3) / 4 * 4;
-  const int64_t max_rows = 16 * kMaxTiles;
-  if (r > max_rows) r = max_rows;
-  *rows_per_wg = r;
-  *tiles = static_cast<int>((r + 15) / 16);
-  *gmax = static_cast<int>(g);
-  return true;
-}
-
 hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                               const void* wq, const float* ws, void* c, hipStream_t stream) {
   const GemmArgs a{m, n, k, aq, as, wq, ws, c, stream};

@@ -11,11 +11,6 @@
 
 namespace fp8bq {
 
-// Row-range launch shape for (N, K): rows per workgroup, tiles, groups per
-// wave (defined in gemm.hip). Returns false when the shape is outside the
-// compiled tables.
-bool rows_shape(int64_t n, int64_t k, int64_t* rows_per_wg, int* tiles, int* gmax);
-
 namespace {
 
 constexpr int kNumCUs = 256;   // MI355X
@@ -34,6 +29,29 @@ struct GemmArgs {
 };
 
 using Launch = hipError_t (*)(const GemmArgs&, int64_t rows_per_wg);
+
+// Row-range launch shape for (N, K): rows per workgroup, tiles, groups
+// per wave. Returns false when the shape is outside the compiled table.
+inline bool rows_shape(int64_t n, int64_t k, int64_t* rows_per_wg, int* tiles, int* gmax) {
+  const int64_t groups = k / kGroup;
+  const int64_t g = (groups + kRowsWaves - 1) / kRowsWaves;
+  if (g < 1 || g > kMaxGroupsPerWave) return false;
+  // Rows per workgroup: N spread over one round of kNumCUs workgroups, or,
+  // when that would exceed the largest tile count, over the fewest whole
+  // rounds that fit (e.g. a vocabulary projection of 152064 rows: 8 rounds
+  // of 76 rows instead of 7.4 rounds of 80, whose last round would leave
+  // most CUs idle).
+  const int64_t max_rows = 16 * kMaxTiles;
+  const int64_t rounds = (n + kNumCUs * max_rows - 1) / (kNumCUs * max_rows);
+  int64_t r = (n + kNumCUs * rounds - 1) / (kNumCUs * rounds);
+  r = (r + 3) / 4 * 4;
+  if (r > max_rows) r = max_rows;
+  *rows_per_wg = r;
+  *tiles = static_cast<int>((r + 15) / 16);
+  *gmax = static_cast<int>(g);
+  return true;
+}
+
 
 template <int MT, int AF, int TILES, int GMAX, int TOK = 16>
 hipError_t rows_instance(const GemmArgs& a, int64_t rows_per_wg) {

@@ -12,8 +12,8 @@ import pytest
 import torch
 
 import memory_bound_w8a8_amd as fp8bq
-from helpers import BF16_U, RMS_TOL, to_gpu
-from oracle import gemm_ref, quant_act_ref, quant_weight_ref, rescore_ref, topk_ref
+from helpers import BF16_U, RMS_TOL, assert_gemm_close, bf16_to_f64, to_gpu
+from oracle import gemm_ref, gemm_ref_at, quant_act_ref, quant_weight_ref, rescore_ref, topk_ref
 import workloads
 
 pytestmark = pytest.mark.gpu
@@ -210,3 +210,28 @@ def test_two_stage_pipeline(m, v, kdim, k):
         # the pick: a survivor whose exact score is within the bound of the best survivor's
         assert pick[r] in idx[r]
         assert exact[r, pick[r]] >= exact[r, idx[r]].max() - 2 * bound.max()
+
+
+def test_coarse_logits_vocabulary_size_sampled():
+    # stage 1 at the full vocabulary size (V = 152064 rows: the row-range
+    # kernel runs several rounds of workgroups), fused quantisation + GEMM,
+    # against the oracle on sampled weight row blocks and all tokens
+    v, kdim = workloads.VOCAB, workloads.HIDDEN
+    w_q, w_s = fp8bq.quant_weight(to_gpu(workloads.weight(v, kdim)))
+    nb = (v + 127) // 128
+    rng = np.random.default_rng(11)
+    blocks = sorted({0, nb - 1, *rng.integers(0, nb, size=4).tolist()})
+    ow = [quant_weight_ref(workloads.weight_block(v, kdim, b)) for b in blocks]
+    wq_cat = np.concatenate([oq for oq, _ in ow])
+    ws_cat = np.concatenate([os_ for _, os_ in ow])
+    cols_local = np.concatenate([128 * i + np.arange(oq.shape[0]) for i, (oq, _) in enumerate(ow)])
+    cols_global = np.concatenate([128 * b + np.arange(oq.shape[0]) for b, (oq, _) in zip(blocks, ow)])
+    for m in (1, 4, 16):
+        h = workloads.activation(m, v, kdim)
+        logits = fp8bq.gemm_fused(to_gpu(h), w_q, w_s)
+        torch.cuda.synchronize()
+        a_q, a_s = quant_act_ref(h.float().numpy())
+        rr, cc = np.meshgrid(np.arange(m), np.arange(len(cols_local)), indexing="ij")
+        ref = gemm_ref_at(a_q, a_s, wq_cat, ws_cat, rr.ravel(), cols_local[cc.ravel()])
+        got = bf16_to_f64(logits[:, torch.from_numpy(cols_global).to(logits.device)]).ravel()
+        assert_gemm_close(got, ref, what=f"coarse logits M={m} V={v}")
