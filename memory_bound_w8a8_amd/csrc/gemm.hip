@@ -40,12 +40,13 @@ hipError_t rows64_instance(const GemmArgs& a, int64_t rows_per_wg) {
 
 // Token classes: up to 8 tokens (16-token tile, operand loaded directly),
 // 9..16 and 17..32 (16- and 32-token tiles, activation read as whole lines
-// and transposed), both holding the activation of all a wave's groups in
-// registers, which for 32 tokens fits up to 6 groups; 32 tokens with more
-// groups, and 33..64 tokens, run the group-major kernel.
+// and transposed; the 32-token tile walks the chunks group-major when a
+// wave has more than 6 groups, so that only the groups in use are held --
+// with up to 2 row tiles; with more, those registers still do not fit and
+// the 64-token kernel serves), and 33..64 tokens (gemm_rows64.h).
 template <int TT, int TILES, int GMAX>
 constexpr Launch rows_entry() {
-  if constexpr (TT == 64 || (TT == 32 && GMAX > 6))
+  if constexpr (TT == 64 || (TT == 32 && GMAX > 6 && TILES > 2))
     return &rows64_instance<TILES, GMAX>;
   else if constexpr (TT == 8)
     return &rows_instance<16, kActCodes, TILES, GMAX>;

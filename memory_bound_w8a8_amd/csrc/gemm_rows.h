@@ -225,10 +225,14 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
   constexpr bool COMPACT = BF16 && TOK < 16;
   static_assert(!BF16 || MT == 16, "in-kernel quantisation serves one 16-token tile");
   // Chunk order. Tile-major (all groups of tile 0, then tile 1, ...) keeps
-  // one accumulator set; with in-kernel quantisation the order is
-  // group-major instead, so that each group's quantisation (at its first
-  // chunk) falls every TILES chunks rather than all within the first tile.
-  constexpr bool GROUP_MAJOR = BF16;
+  // one accumulator set but holds the activation of all the wave's groups
+  // in registers for the whole kernel; group-major (all tiles of group 0,
+  // then group 1, ...) holds one accumulator set per tile and only the
+  // groups in use, loaded with their group's first weight chunk. Group-major
+  // serves in-kernel quantisation (each group's quantisation then falls
+  // every TILES chunks rather than all within the first tile) and 32-token
+  // tiles with more than 6 groups per wave (whose activation would not fit).
+  constexpr bool GROUP_MAJOR = BF16 || (LINES && MT == 32 && GMAX > 6);
   constexpr int MS = KC::kMS;
   constexpr int CH = KC::kChunks;
   constexpr int RING = KC::kRing;
@@ -288,39 +292,53 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
   } else if constexpr (BF16) {
     const int tok = lrow < m_rows ? lrow : m_rows - 1;
     arow = reinterpret_cast<const unsigned short*>(aq) + static_cast<int64_t>(tok) * k + 16 * quarter;
-  } else {
+  }
+  // Activation codes (and scales) of group u for every 16-token tile, as
+  // whole lines (LINES) or as the operand directly.
+  const unsigned char* ap0[MS];
+  const unsigned char* ap1[MS];
+  const float* sap[MS];
+  bool mval[MS];
+  if constexpr (!BF16) {
 #pragma unroll
-  for (int s = 0; s < MS; ++s) {
-    const unsigned char* ap0;
-    const unsigned char* ap1;
-    if constexpr (LINES) {
-      int m0 = 16 * s + lr8;
-      int m1 = m0 + 8;
-      m0 = m0 < m_rows ? m0 : m_rows - 1;
-      m1 = m1 < m_rows ? m1 : m_rows - 1;
-      ap0 = aq + static_cast<int64_t>(m0) * k + piece * 16;
-      ap1 = aq + static_cast<int64_t>(m1) * k + piece * 16;
-    } else {
-      int m0 = 16 * s + lrow;
-      m0 = m0 < m_rows ? m0 : m_rows - 1;
-      ap0 = aq + static_cast<int64_t>(m0) * k + quarter * 16;
-      ap1 = ap0 + 64;
-    }
-    const int m = 16 * s + lrow;
-    const bool mval = m < m_rows;
-    const float* sap = as + static_cast<int64_t>(mval ? m : m_rows - 1) * groups;
-#pragma unroll
-    for (int u = 0; u < GMAX; ++u) {
-      const bool live = u < gcnt;
-      const int g = live ? gbeg + u : glast;
-      const int64_t off = static_cast<int64_t>(g) * kGroup;
-      const v4u lo = *reinterpret_cast<const v4u*>(ap0 + off);
-      const v4u hi = *reinterpret_cast<const v4u*>(ap1 + off);
-      bv[u][s] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-      const float scale = sap[g];
-      sa[u][s] = (live && mval) ? scale : 0.f;
+    for (int s = 0; s < MS; ++s) {
+      if constexpr (LINES) {
+        int m0 = 16 * s + lr8;
+        int m1 = m0 + 8;
+        m0 = m0 < m_rows ? m0 : m_rows - 1;
+        m1 = m1 < m_rows ? m1 : m_rows - 1;
+        ap0[s] = aq + static_cast<int64_t>(m0) * k + piece * 16;
+        ap1[s] = aq + static_cast<int64_t>(m1) * k + piece * 16;
+      } else {
+        int m0 = 16 * s + lrow;
+        m0 = m0 < m_rows ? m0 : m_rows - 1;
+        ap0[s] = aq + static_cast<int64_t>(m0) * k + quarter * 16;
+        ap1[s] = ap0[s] + 64;
+      }
+      const int m = 16 * s + lrow;
+      mval[s] = m < m_rows;
+      sap[s] = as + static_cast<int64_t>(mval[s] ? m : m_rows - 1) * groups;
     }
   }
+  auto load_act_tile = [&](int u, int s) {
+    const bool live = u < gcnt;
+    const int g = live ? gbeg + u : glast;
+    const int64_t off = static_cast<int64_t>(g) * kGroup;
+    const v4u lo = *reinterpret_cast<const v4u*>(ap0[s] + off);
+    const v4u hi = *reinterpret_cast<const v4u*>(ap1[s] + off);
+    bv[u][s] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    const float scale = sap[s][g];
+    sa[u][s] = (live && mval[s]) ? scale : 0.f;
+  };
+  auto load_act = [&](int u) {
+#pragma unroll
+    for (int s = 0; s < MS; ++s) load_act_tile(u, s);
+  };
+  if constexpr (!BF16 && !GROUP_MAJOR) {
+#pragma unroll
+    for (int s = 0; s < MS; ++s)
+#pragma unroll
+      for (int u = 0; u < GMAX; ++u) load_act_tile(u, s);
   }
 
   v8i wv[RING];
@@ -330,6 +348,7 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     const int t = GROUP_MAJOR ? ci % TILES : ci / GMAX;
     const int u = GROUP_MAJOR ? ci / TILES : ci % GMAX;
     const int g = u < gcnt ? gbeg + u : glast;
+    if (GROUP_MAJOR && !BF16 && t == 0) load_act(u);
     if (BF16 && t == 0) {
       const unsigned short* p = arow + static_cast<int64_t>(g) * kGroup;
       if constexpr (COMPACT) {  // 2 TOK bf16 values of one token
@@ -392,11 +411,11 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     const int t = GROUP_MAJOR ? ci % TILES : ci / GMAX;
     const int u = GROUP_MAJOR ? ci / TILES : ci % GMAX;
     v4f (&at)[MS] = acc[GROUP_MAJOR ? t : 0];
-    // With many groups per wave and in-kernel quantisation, keep the
+    // With many groups per wave in group-major order, keep the
     // scheduler from hoisting later chunks' loads (and the activation
     // values they bring) above this one: their registers would outgrow the
     // budget and spill.
-    if constexpr (BF16 && GMAX >= 7) __builtin_amdgcn_sched_barrier(0);
+    if constexpr (GROUP_MAJOR && GMAX >= 7) __builtin_amdgcn_sched_barrier(0);
     if (ci + PD < CH) load_chunk(ci + PD, (ci + PD) % RING);
     if (!GROUP_MAJOR && u == 0) {
 #pragma unroll

@@ -63,7 +63,7 @@ def test_odd_shapes(m, n, k):
 # -> 16-row tiles 1..5, K groups per wave 1..9, a K past the table (generic
 # kernel), N not a multiple of 4, and workgroups whose last tile is short.
 TABLE_SHAPES = [(1000, 9216), (12800, 1024), (20000, 2304), (4100, 5120), (5000, 9344), (300, 8704),
-                (1026, 256), (7, 1280), (2999, 3072)]
+                (1026, 256), (7, 1280), (2999, 3072), (6000, 8704), (5120, 7168), (9000, 8704)]
 
 
 @pytest.mark.parametrize("n,k", TABLE_SHAPES)
@@ -103,6 +103,18 @@ def test_integer_exact_bitwise_k1024(m):
     c = _gpu_gemm(a_q, a_s, w_q, w_s)
     want = bf16_rne(gemm_ref(a_q, a_s, w_q, w_s))
     assert np.array_equal(c, want)
+
+
+@pytest.mark.parametrize("m", [1, 17, 24, 32])
+def test_integer_exact_bitwise_k8704(m):
+    # 68 groups: 9 per wave, where 17..32 tokens walk the chunks group-major
+    # (and, past 2 row tiles, run the 64-token kernel); |codes| <= 2,
+    # scales in {1, 2}: group sums < 2^10, running sums < 2^18, exact.
+    for n in (5120, 9000):
+        a_q, a_s, w_q, w_s = _integer_problem(m, n, 8704, 2, [1.0, 2.0], seed=200 + m)
+        c = _gpu_gemm(a_q, a_s, w_q, w_s)
+        want = bf16_rne(gemm_ref(a_q, a_s, w_q, w_s))
+        assert np.array_equal(c, want), f"M={m} N={n}"
 
 
 @pytest.mark.parametrize("m", [1, 3, 8, 64, 130])
@@ -159,6 +171,8 @@ def _full_cases():
         ms = [1, 8, 64]
         if (n, k) == (17408, 5120):
             ms = list(range(1, 9)) + [16, 32, 64]
+        if (n, k) == (5120, 8704):
+            ms = [1, 8, 17, 32, 64]
         if (n, k) in workloads.PREFILL_SHAPES:
             ms.append(workloads.PREFILL_M)
         cases += [(m, n, k) for m in ms]
