@@ -286,6 +286,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
           acc[i][j - 1][1] = fmaf(sc_prev, p_prev[i][1], acc[i][j - 1][1]);
           acc[i][j - 1][2] = fmaf(sc_prev, p_prev[i][2], acc[i][j - 1][2]);
           acc[i][j - 1][3] = fmaf(sc_prev, p_prev[i][3], acc[i][j - 1][3]);
+          // Pin the update here: left free, the compiler sinks every FMA of
+          // the step below the step's closing barrier, where both waves of
+          // a SIMD run them at once while the matrix core idles.
+          asm volatile("" : "+v"(acc[i][j - 1]));
         }
         // Keep this order: left alone, the compiler issues all MFMAs of the
         // step first and all FMAs afterwards, so that the matrix core and
@@ -304,6 +308,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
       acc[i][J - 1][1] = fmaf(sc_prev, p_prev[i][1], acc[i][J - 1][1]);
       acc[i][J - 1][2] = fmaf(sc_prev, p_prev[i][2], acc[i][J - 1][2]);
       acc[i][J - 1][3] = fmaf(sc_prev, p_prev[i][3], acc[i][J - 1][3]);
+      asm volatile("" : "+v"(acc[i][J - 1]));
     }
 
     // Step g + 1's copies must have landed, and every wave must be done
