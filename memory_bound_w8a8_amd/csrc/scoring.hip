@@ -271,8 +271,24 @@ __global__ __launch_bounds__(64 * kRescoreWaves) void rescore_kernel(int64_t kdi
   const v4u* wrow = reinterpret_cast<const v4u*>(w + static_cast<int64_t>(r) * kdim);
   const int64_t pieces = kdim >> 3;
   float acc = 0.f;
-#pragma unroll 8
-  for (int64_t i = lane; i < pieces; i += 64) acc = dot8(hrow[i], __builtin_nontemporal_load(wrow + i), acc);
+  // Batches of kBatch pieces per lane: every load of a batch is issued
+  // before the first product waits (K up to 6144 is one memory round trip),
+  // then the products are accumulated in piece order as before.
+  constexpr int kBatch = 12;
+  for (int64_t base = lane; base < pieces; base += 64 * kBatch) {
+    v4u hv[kBatch], wv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t i = base + 64 * u;
+      if (i < pieces) {
+        hv[u] = hrow[i];
+        wv[u] = __builtin_nontemporal_load(wrow + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (base + 64 * u < pieces) acc = dot8(hv[u], wv[u], acc);
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) scores[row * k + j] = acc;
