@@ -85,7 +85,7 @@ __device__ __forceinline__ void wave_max_min(unsigned v, unsigned* vmax, unsigne
 // equal keys by lower position -- to dst[0 .. k) in position order, padded
 // with empty entries when fewer than k are not empty. One whole wave calls it.
 template <int PER>
-__device__ void wave_select(const unsigned (&key)[PER], const unsigned (&idx)[PER], int k, v2u* dst) {
+__device__ __forceinline__ void wave_select(const unsigned (&key)[PER], const unsigned (&idx)[PER], int k, v2u* dst) {
   const int lane = threadIdx.x & 63;
   // t: the largest key with at least k candidates at or above it (1 when
   // fewer than k candidates are not empty). It lies in [lo, hi): hi is one
@@ -131,20 +131,35 @@ __device__ void wave_select(const unsigned (&key)[PER], const unsigned (&idx)[PE
 // The k best of the n (<= 1024) candidates src[0 .. n) (position order),
 // written to dst as wave_select does. One whole wave calls it.
 template <int PER>
-__device__ void select_from(const v2u* src, int n, int k, v2u* dst) {
+__device__ __forceinline__ void select_from(const v2u* src, int n, int k, v2u* dst) {
   const int lane = threadIdx.x & 63;
   unsigned key[PER], idx[PER];
+  // every load in bounds (index clamped to n - 1) and unconditional, so the
+  // PER loads are in flight together; positions past n become empty
+  const int last = n > 0 ? n - 1 : 0;
+  v2u e[PER];
+  if (n > 0) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int p = 64 * r + lane;
+      e[r] = src[p < n ? p : last];
+    }
+#pragma unroll
+    for (int r = 0; r < PER; ++r) asm volatile("" : "+v"(e[r]));
+  } else {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) e[r] = v2u{0u, 0u};
+  }
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
     const int p = 64 * r + lane;
-    const v2u e = p < n ? src[p] : v2u{0u, 0u};
-    key[r] = e[0];
-    idx[r] = e[1];
+    key[r] = p < n ? e[r][0] : 0u;
+    idx[r] = e[r][1];
   }
   wave_select<PER>(key, idx, k, dst);
 }
 
-__device__ void select_list(const v2u* src, int n, int k, v2u* dst) {
+__device__ __forceinline__ void select_list(const v2u* src, int n, int k, v2u* dst) {
   if (n <= 256) {
     select_from<4>(src, n, k, dst);
   } else {
@@ -155,7 +170,7 @@ __device__ void select_list(const v2u* src, int n, int k, v2u* dst) {
 // sel[0 .. k): a row's k best in position order (all non-empty). Writes them
 // ordered by (key descending, position ascending): each entry's slot is the
 // number of entries ranked above it. One whole wave calls it.
-__device__ void wave_place(const v2u* sel, int k, int* __restrict__ out_idx, unsigned short* __restrict__ out_val) {
+__device__ __forceinline__ void wave_place(const v2u* sel, int k, int* __restrict__ out_idx, unsigned short* __restrict__ out_val) {
   const int lane = threadIdx.x & 63;
   for (int i = lane; i < k; i += 64) {
     const v2u e = sel[i];
@@ -184,10 +199,22 @@ __global__ __launch_bounds__(64 * kMaxGroup) void topk_chunk_kernel(int64_t v, i
   const int64_t base = (static_cast<int64_t>(part) * group + wave) * kWaveCand;
   const unsigned short* x = logits + row * v;
   unsigned key[kPer], idx[kPer];
+  // loads from clamped (in-bounds) positions, all issued before any is
+  // used (the empty asm keeps the compiler from moving each load into a
+  // branch on pos < v, which would wait for the loads one at a time);
+  // positions past the row become empty
+  unsigned raw[kPer];
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int64_t pos = base + 64 * r + lane;
-    key[r] = pos < v ? key16(x[pos]) + 1u : 0u;
+    raw[r] = x[pos < v ? pos : v - 1];
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) asm volatile("" : "+v"(raw[r]));
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int64_t pos = base + 64 * r + lane;
+    key[r] = pos < v ? key16(raw[r]) + 1u : 0u;
     idx[r] = static_cast<unsigned>(pos);
   }
   wave_select<kPer>(key, idx, k, wave_lists + wave * k);
