@@ -94,8 +94,12 @@ int fp8bq_quant_weight(int64_t N, int64_t K, const float *W_f32, void *W_fp8, fl
  *   A_fp8    [M, K] uint8 codes,  A_scales [M, K/128] fp32          (read)
  *   W_fp8    [N, K] uint8 codes,  W_scales [ceil(N/128), K/128] fp32 (read)
  *   C_bf16   [M, N] bf16, written, fp32 accumulation rounded to bf16 RNE.
- * Every M >= 1 is served by a kernel chosen from explicit M ranges (no
- * nearest-size table). The summation order differs from the fp64
+ * Every M >= 1 is served by a kernel chosen from explicit ranges (no
+ * nearest-size table): M <= 64 streams the weights once; 65 <= M <= 128
+ * streams them twice (tokens 0..63, then the rest) when N <= 16256 (where
+ * the tiled kernel's grid of ceil(N / 128) workgroups would fill under half
+ * the 256 CUs); the LDS-tiled MFMA kernel otherwise. The summation order
+ * differs from the fp64
  * definition; results agree within fp32 accumulation plus bf16 rounding.
  * Two identical calls give bitwise-identical C (no atomics).
  * K == 0 writes zeros. Errors: NULL pointer; negative size; K % 128 != 0;
@@ -109,7 +113,7 @@ int fp8bq_gemm(int64_t M, int64_t N, int64_t K, const void *A_fp8, const float *
 /*
  * Kernel-path introspection for tests and profiling. Returns the path
  * fp8bq_gemm would take for (M, N, K) -- FP8BQ_PATH_STREAM for the
- * weight-streaming split-K kernel, FP8BQ_PATH_TILED for the LDS-tiled MFMA
+ * weight-streaming split-K kernels, FP8BQ_PATH_TILED for the LDS-tiled MFMA
  * kernel -- or a negative status for invalid sizes.
  */
 enum { FP8BQ_PATH_NONE = 0, FP8BQ_PATH_STREAM = 1, FP8BQ_PATH_TILED = 2 };
@@ -117,8 +121,8 @@ int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K);
 
 /*
  * fp8bq_gemm with the kernel path forced (FP8BQ_PATH_STREAM requires
- * M <= 64; FP8BQ_PATH_TILED accepts any M). For cross-checking the two paths
- * at the same M. Same arguments, semantics and errors as fp8bq_gemm, plus
+ * M <= 128, as two launches past 64 tokens; FP8BQ_PATH_TILED accepts any
+ * M). For cross-checking the two paths at the same M. Same arguments, semantics and errors as fp8bq_gemm, plus
  * FP8BQ_ERR_SHAPE for a path that cannot serve M.
  */
 int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_fp8,

@@ -208,7 +208,7 @@ def gemm_fused(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
 
 
 def gemm_forced(path: int, a_q, a_s, w_q, w_s, out=None) -> torch.Tensor:
-    """gemm() on a chosen kernel path (PATH_STREAM needs M <= 64)."""
+    """gemm() on a chosen kernel path (PATH_STREAM needs M <= 128)."""
     a_q, w_q, m, n, k, out = _gemm_args(a_q, a_s, w_q, w_s, out)
     with torch.cuda.device(a_q.device):
         st = lib().fp8bq_gemm_forced(int(path), m, n, k, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(out),

@@ -11,7 +11,9 @@
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // bound on M*K, N*K, M*N
-constexpr int64_t kStreamMaxM = 64;              // streaming kernel serves 1..64
+constexpr int64_t kStreamMaxM = 64;              // streaming kernels serve 1..64 tokens per launch
+constexpr int64_t kStreamSplitMaxM = 128;        // ... and 65..128 as two launches (64 + the rest)
+constexpr int64_t kStreamSplitMaxTiles = 128;    // ... where the tiled kernel would fill under half the CUs
 constexpr int64_t kTiledMaxK = int64_t(1) << 24; // tiled kernel: 32-bit offsets within a 256-row tile
 constexpr int kMaxDevices = 64;
 constexpr int64_t kSmallMaxM = 16;               // fused and weight-only paths: one 16-token tile
@@ -58,13 +60,31 @@ int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A_fp8, const fl
   return FP8BQ_OK;
 }
 
-int gemm_path(int64_t M) { return M <= kStreamMaxM ? FP8BQ_PATH_STREAM : FP8BQ_PATH_TILED; }
+// 1..64 tokens stream the weights once; 65..128 tokens also stream (twice:
+// tokens 0..63, then the rest) when the tiled kernel's grid, one workgroup
+// per 128 weight rows at this M, would leave more than half the CUs idle;
+// otherwise, and beyond 128 tokens, the tiled kernel.
+int gemm_path(int64_t M, int64_t N) {
+  if (M <= kStreamMaxM) return FP8BQ_PATH_STREAM;
+  if (M <= kStreamSplitMaxM && (N + 127) / 128 < kStreamSplitMaxTiles) return FP8BQ_PATH_STREAM;
+  return FP8BQ_PATH_TILED;
+}
+
+hipError_t launch_stream_split(int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales,
+                               const void* W_fp8, const float* W_scales, void* C_bf16, hipStream_t s) {
+  if (M <= kStreamMaxM) return fp8bq::launch_gemm_stream(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s);
+  const hipError_t e = fp8bq::launch_gemm_stream(kStreamMaxM, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s);
+  if (e != hipSuccess) return e;
+  return fp8bq::launch_gemm_stream(M - kStreamMaxM, N, K, static_cast<const unsigned char*>(A_fp8) + kStreamMaxM * K,
+                                   A_scales + kStreamMaxM * (K / 128), W_fp8, W_scales,
+                                   static_cast<unsigned short*>(C_bf16) + kStreamMaxM * N, s);
+}
 
 int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales,
              const void* W_fp8, const float* W_scales, void* C_bf16, void* stream) {
   int st = check_gemm_args(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16);
   if (st != FP8BQ_OK) return st;
-  if (path == FP8BQ_PATH_STREAM && M > kStreamMaxM) return FP8BQ_ERR_SHAPE;
+  if (path == FP8BQ_PATH_STREAM && M > kStreamSplitMaxM) return FP8BQ_ERR_SHAPE;
   if (path == FP8BQ_PATH_TILED && K >= kTiledMaxK) return FP8BQ_ERR_SHAPE;
   if (path != FP8BQ_PATH_STREAM && path != FP8BQ_PATH_TILED) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_OK;
@@ -73,7 +93,7 @@ int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) return launch_status(fp8bq::launch_fill_zero_bf16(M * N, C_bf16, s));
   if (path == FP8BQ_PATH_STREAM)
-    return launch_status(fp8bq::launch_gemm_stream(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s));
+    return launch_status(launch_stream_split(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s));
   return launch_status(fp8bq::launch_gemm_tiled(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s));
 }
 
@@ -104,8 +124,8 @@ int fp8bq_quant_weight(int64_t N, int64_t K, const float* W_f32, void* W_fp8, fl
 
 int fp8bq_gemm(int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales, const void* W_fp8,
                const float* W_scales, void* C_bf16, void* stream) {
-  if (M < 0) return FP8BQ_ERR_SHAPE;
-  return run_gemm(gemm_path(M), M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
+  if (M < 0 || N < 0) return FP8BQ_ERR_SHAPE;
+  return run_gemm(gemm_path(M, N), M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
 }
 
 int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales,
@@ -117,7 +137,7 @@ int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
   if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_PATH_NONE;
-  return gemm_path(M);
+  return gemm_path(M, N);
 }
 
 int fp8bq_gemm_fused(int64_t M, int64_t N, int64_t K, const void* A_bf16, const void* W_fp8, const float* W_scales,

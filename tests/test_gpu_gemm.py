@@ -127,7 +127,7 @@ def test_integer_exact_bitwise_k5120(m):
     assert np.array_equal(c, want)
 
 
-@pytest.mark.parametrize("m", [1, 4, 8, 16, 33, 64])
+@pytest.mark.parametrize("m", [1, 4, 8, 16, 33, 64, 65, 100, 128])
 def test_stream_and_tiled_paths_agree(m):
     a_q, a_s, w_q, w_s = _problem(m, 1024, 2048)
     ref = gemm_ref(a_q, a_s, w_q, w_s)
@@ -172,7 +172,9 @@ def _full_cases():
         if (n, k) == (17408, 5120):
             ms = list(range(1, 9)) + [16, 32, 64]
         if (n, k) == (5120, 8704):
-            ms = [1, 8, 17, 32, 64]
+            ms = [1, 8, 17, 32, 64, 65, 128]
+        if (n, k) == (7168, 5120):
+            ms = [1, 8, 64, 100]
         if (n, k) in workloads.PREFILL_SHAPES:
             ms.append(workloads.PREFILL_M)
         cases += [(m, n, k) for m in ms]
