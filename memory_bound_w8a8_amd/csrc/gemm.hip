@@ -151,11 +151,15 @@ hipError_t tiled_instance(int64_t m, int64_t n, int64_t k, const void* aq, const
 
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                              const void* wq, const float* ws, void* c, hipStream_t stream) {
-  // Up to 128 tokens there is one token tile, so the workgroup count is the
-  // number of weight tiles: 128 x 128 tiles of 4 waves (twice as many
-  // workgroups as 128 x 256) measured 1.3-1.6x faster there; beyond, 128
-  // tokens x 256 weight rows per 8-wave workgroup (2 x 4 waves of 64 x 64).
-  if (m <= 128) return tiled_instance<128, 128, 2, 2>(m, n, k, aq, as, wq, ws, c, stream);
+  // 128 x 128 tiles of 4 waves while their grid fits one round of
+  // workgroups on the 256 CUs: twice the workgroups of 128 x 256 tiles,
+  // measured 1.3-1.6x faster there (every M <= 128 on the five weight
+  // shapes; up to 512-768 tokens on N = 5120..8192); a grid that would
+  // spill into a second, partly empty round is slower than the wider tiles.
+  // Otherwise 128 tokens x 256 weight rows per 8-wave workgroup (2 x 4 waves
+  // of 64 x 64).
+  const int64_t narrow_tiles = ((m + 127) / 128) * ((n + 127) / 128);
+  if (narrow_tiles <= kNumCUs) return tiled_instance<128, 128, 2, 2>(m, n, k, aq, as, wq, ws, c, stream);
   return tiled_instance<128, 256, 2, 4>(m, n, k, aq, as, wq, ws, c, stream);
 }
 
