@@ -11,6 +11,7 @@
 // table (very large K) run the generic streaming kernel, which handles any
 // size with runtime loops.
 #include <array>
+#include <string>
 #include <utility>
 
 #include "device_common.h"
@@ -108,6 +109,12 @@ __global__ void fill_zero_kernel(unsigned short* __restrict__ c, int64_t count) 
 
 }  // namespace
 
+// Description of a row-range launch for the kernel-choice log.
+static std::string rows_desc(const char* kernel, int64_t n, int64_t rows_per_wg, int tiles, int gmax) {
+  return std::string(kernel) + " TILES=" + std::to_string(tiles) + " GMAX=" + std::to_string(gmax) +
+         " rows/wg=" + std::to_string(rows_per_wg) + " grid=" + std::to_string((n + rows_per_wg - 1) / rows_per_wg);
+}
+
 hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                               const void* wq, const float* ws, void* c, hipStream_t stream) {
   const GemmArgs a{m, n, k, aq, as, wq, ws, c, stream};
@@ -115,9 +122,15 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
   int tiles, gmax;
   if (rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) {
     const auto& table = m <= 8 ? kRows8 : m <= 16 ? kRows16 : m <= 32 ? kRows32 : kRows64;
+    const char* kernel = m <= 8    ? "gemm_rows_kernel MT=16 act=codes"
+                         : m <= 16 ? "gemm_rows_kernel MT=16 act=lines"
+                         : m <= 32 ? (gmax > 6 && tiles > 2 ? "gemm_rows64_kernel" : "gemm_rows_kernel MT=32 act=lines")
+                                   : "gemm_rows64_kernel";
+    dispatch_log("gemm(stream)", m, n, k, rows_desc(kernel, n, rows_per_wg, tiles, gmax).c_str());
     return table[tiles - 1][gmax - 1](a, rows_per_wg);
   }
   // Generic streaming kernel: any N and K, 16-row slabs, runtime K loop.
+  dispatch_log("gemm(stream)", m, n, k, "gemm_stream_kernel (generic: K beyond the instance table)");
   if (m <= 16) return stream_instance<16, 1, 8, 5>(a);
   if (m <= 32) return stream_instance<32, 1, 8, 4>(a);
   return stream_instance<64, 1, 8, 2>(a);
@@ -135,6 +148,7 @@ hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, con
   int64_t rows_per_wg;
   int tiles, gmax;
   if (m < 1 || m > 16 || !rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) return hipErrorInvalidValue;
+  dispatch_log("gemm_w8a16", m, n, k, rows_desc("gemm_w8a16_kernel", n, rows_per_wg, tiles, gmax).c_str());
   return kW8A16[tiles - 1][gmax - 1](args, rows_per_wg);
 }
 
@@ -159,7 +173,14 @@ hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, co
   // Otherwise 128 tokens x 256 weight rows per 8-wave workgroup (2 x 4 waves
   // of 64 x 64).
   const int64_t narrow_tiles = ((m + 127) / 128) * ((n + 127) / 128);
-  if (narrow_tiles <= kNumCUs) return tiled_instance<128, 128, 2, 2>(m, n, k, aq, as, wq, ws, c, stream);
+  if (narrow_tiles <= kNumCUs) {
+    dispatch_log("gemm(tiled)", m, n, k,
+                 ("gemm_tiled_kernel BM=128 BN=128 4 waves grid=" + std::to_string(narrow_tiles)).c_str());
+    return tiled_instance<128, 128, 2, 2>(m, n, k, aq, as, wq, ws, c, stream);
+  }
+  dispatch_log("gemm(tiled)", m, n, k,
+               ("gemm_tiled_kernel BM=128 BN=256 8 waves grid=" + std::to_string(((m + 127) / 128) * ((n + 255) / 256)))
+                   .c_str());
   return tiled_instance<128, 256, 2, 4>(m, n, k, aq, as, wq, ws, c, stream);
 }
 

@@ -10,6 +10,7 @@
 // tokens quantise in the MFMA operand layout directly. Every M inside a
 // class runs the same instruction stream.
 #include <array>
+#include <string>
 #include <utility>
 
 #include "launch.h"
@@ -44,6 +45,12 @@ hipError_t launch_gemm_fused(int64_t m, int64_t n, int64_t k, const void* a, con
   int tiles, gmax;
   if (m < 1 || m > 16 || !rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) return hipErrorInvalidValue;
   const auto& table = m == 1 ? kFused1 : m == 2 ? kFused2 : m <= 4 ? kFused4 : m <= 8 ? kFused8 : kFused16;
+  const int tok = m == 1 ? 1 : m == 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
+  dispatch_log("gemm_fused", m, n, k,
+               ("gemm_rows_kernel MT=16 act=bf16 TOK=" + std::to_string(tok) + " TILES=" + std::to_string(tiles) +
+                " GMAX=" + std::to_string(gmax) + " rows/wg=" + std::to_string(rows_per_wg) +
+                " grid=" + std::to_string((n + rows_per_wg - 1) / rows_per_wg))
+                   .c_str());
   return table[tiles - 1][gmax - 1](args, rows_per_wg);
 }
 

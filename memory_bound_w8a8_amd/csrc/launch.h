@@ -41,6 +41,10 @@ hipError_t launch_topk(int64_t m, int64_t v, int k, const void* logits, void* wo
 hipError_t launch_rescore(int64_t m, int64_t kdim, int64_t v, int64_t k, const void* h, const void* w,
                           const int* idx, float* scores, int* pick, hipStream_t stream);
 
+// Kernel-choice log (FP8BQ_LOG=1): prints each distinct (entry, M, N, K)
+// -> kernel description once to stderr; a no-op otherwise.
+void dispatch_log(const char* entry, int64_t m, int64_t n, int64_t k, const char* kernel);
+
 // C = 0 (used for K == 0).
 hipError_t launch_fill_zero_bf16(int64_t count, void* c, hipStream_t stream);
 

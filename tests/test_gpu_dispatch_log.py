@@ -1,0 +1,45 @@
+"""The kernel-choice log (FP8BQ_LOG=1): each distinct (entry point, M, N,
+K) decision is printed once, naming the instance the shape's M range and
+(N, K) select. Runs one child process (the variable is read once per
+process)."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.gpu
+
+CHILD = r"""
+import torch
+import memory_bound_w8a8_amd as fp8bq
+dev = torch.device("cuda:0")
+k = 5120
+w_q, w_s = fp8bq.quant_weight(torch.randn(17408, k, device=dev) * 0.02)
+for m in (1, 3, 1, 16, 32, 64, 65, 3465):
+    a_q, a_s = fp8bq.quant_act(torch.randn(m, k, device=dev).to(torch.bfloat16))
+    fp8bq.gemm(a_q, a_s, w_q, w_s)
+fp8bq.gemm_fused(torch.randn(2, k, device=dev).to(torch.bfloat16), w_q, w_s)
+torch.cuda.synchronize()
+"""
+
+
+def test_dispatch_log_names_each_decision_once():
+    env = dict(os.environ, FP8BQ_LOG="1", PYTHONPATH=ROOT)
+    proc = subprocess.run([sys.executable, "-c", CHILD], env=env, cwd=ROOT, capture_output=True, text=True,
+                          timeout=300)
+    assert proc.returncode == 0, proc.stderr[-2000:]
+    lines = [ln for ln in proc.stderr.splitlines() if ln.startswith("fp8bq: ")]
+    assert len(lines) == len(set(lines))  # M = 1 twice: logged once
+    got = {ln.split(" -> ")[0]: ln.split(" -> ")[1] for ln in lines}
+    assert got["fp8bq: gemm(stream) M=1 N=17408 K=5120"].startswith("gemm_rows_kernel MT=16 act=codes TILES=5 GMAX=5")
+    assert "rows/wg=68 grid=256" in got["fp8bq: gemm(stream) M=3 N=17408 K=5120"]
+    assert got["fp8bq: gemm(stream) M=16 N=17408 K=5120"].startswith("gemm_rows_kernel MT=16 act=lines")
+    assert got["fp8bq: gemm(stream) M=32 N=17408 K=5120"].startswith("gemm_rows_kernel MT=32 act=lines")
+    assert got["fp8bq: gemm(stream) M=64 N=17408 K=5120"].startswith("gemm_rows64_kernel")
+    assert got["fp8bq: gemm(tiled) M=65 N=17408 K=5120"].startswith("gemm_tiled_kernel BM=128 BN=128")
+    assert got["fp8bq: gemm(tiled) M=3465 N=17408 K=5120"].startswith("gemm_tiled_kernel BM=128 BN=256")
+    assert got["fp8bq: gemm_fused M=2 N=17408 K=5120"].startswith("gemm_rows_kernel MT=16 act=bf16 TOK=2")
