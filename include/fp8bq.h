@@ -117,12 +117,22 @@ int fp8bq_gemm(int64_t M, int64_t N, int64_t K, const void *A_fp8, const float *
  * kernel -- or a negative status for invalid sizes.
  */
 enum { FP8BQ_PATH_NONE = 0, FP8BQ_PATH_STREAM = 1, FP8BQ_PATH_TILED = 2 };
+/* Tile shapes of the tiled kernel (tokens x weight rows), accepted by
+ * fp8bq_gemm_forced only; FP8BQ_PATH_TILED picks one from (M, N). */
+enum {
+  FP8BQ_PATH_TILED_128x128 = 3,
+  FP8BQ_PATH_TILED_128x256 = 4,
+  FP8BQ_PATH_TILED_192x256 = 5,
+  FP8BQ_PATH_TILED_256x256 = 6
+};
 int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K);
 
 /*
  * fp8bq_gemm with the kernel path forced (FP8BQ_PATH_STREAM requires
- * M <= 128, as two launches past 64 tokens; FP8BQ_PATH_TILED accepts any
- * M). For cross-checking the two paths at the same M. Same arguments, semantics and errors as fp8bq_gemm, plus
+ * M <= 128, as two launches past 64 tokens; FP8BQ_PATH_TILED and the
+ * FP8BQ_PATH_TILED_* shapes accept any M). For cross-checking the paths and
+ * tile shapes at the same M: every tile shape sums each output in the same
+ * order, so their results are bitwise equal. Same arguments, semantics and errors as fp8bq_gemm, plus
  * FP8BQ_ERR_SHAPE for a path that cannot serve M.
  */
 int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_fp8,

@@ -25,6 +25,8 @@ LIB_PATH = os.path.join(_PKG, "libfp8bq.so")
 
 FP8BQ_OK = 0
 PATH_NONE, PATH_STREAM, PATH_TILED = 0, 1, 2
+# tile shapes of the tiled kernel (tokens x weight rows), for gemm_forced
+PATH_TILED_128x128, PATH_TILED_128x256, PATH_TILED_192x256, PATH_TILED_256x256 = 3, 4, 5, 6
 PATH_NAMES = {PATH_NONE: "none", PATH_STREAM: "stream", PATH_TILED: "tiled"}
 
 # Every symbol the C ABI exports (kept in step with include/fp8bq.h).
@@ -208,7 +210,7 @@ def gemm_fused(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
 
 
 def gemm_forced(path: int, a_q, a_s, w_q, w_s, out=None) -> torch.Tensor:
-    """gemm() on a chosen kernel path (PATH_STREAM needs M <= 128)."""
+    """gemm() on a chosen kernel path or tile shape (PATH_STREAM needs M <= 128)."""
     a_q, w_q, m, n, k, out = _gemm_args(a_q, a_s, w_q, w_s, out)
     with torch.cuda.device(a_q.device):
         st = lib().fp8bq_gemm_forced(int(path), m, n, k, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(out),

@@ -84,9 +84,10 @@ int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const
              const void* W_fp8, const float* W_scales, void* C_bf16, void* stream) {
   int st = check_gemm_args(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16);
   if (st != FP8BQ_OK) return st;
+  const bool tiled = path == FP8BQ_PATH_TILED || (path >= FP8BQ_PATH_TILED_128x128 && path <= FP8BQ_PATH_TILED_256x256);
   if (path == FP8BQ_PATH_STREAM && M > kStreamSplitMaxM) return FP8BQ_ERR_SHAPE;
-  if (path == FP8BQ_PATH_TILED && K >= kTiledMaxK) return FP8BQ_ERR_SHAPE;
-  if (path != FP8BQ_PATH_STREAM && path != FP8BQ_PATH_TILED) return FP8BQ_ERR_SHAPE;
+  if (tiled && K >= kTiledMaxK) return FP8BQ_ERR_SHAPE;
+  if (path != FP8BQ_PATH_STREAM && !tiled) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_OK;
   st = check_device();
   if (st != FP8BQ_OK) return st;
@@ -94,7 +95,8 @@ int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const
   if (K == 0) return launch_status(fp8bq::launch_fill_zero_bf16(M * N, C_bf16, s));
   if (path == FP8BQ_PATH_STREAM)
     return launch_status(launch_stream_split(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s));
-  return launch_status(fp8bq::launch_gemm_tiled(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s));
+  const int shape = path == FP8BQ_PATH_TILED ? -1 : path - FP8BQ_PATH_TILED_128x128;
+  return launch_status(fp8bq::launch_gemm_tiled(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s, shape));
 }
 
 }  // namespace

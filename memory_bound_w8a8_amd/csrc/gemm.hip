@@ -11,6 +11,7 @@
 // table (very large K) run the generic streaming kernel, which handles any
 // size with runtime loops.
 #include <array>
+#include <cstdint>
 #include <string>
 #include <utility>
 
@@ -152,10 +153,9 @@ hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, con
   return kW8A16[tiles - 1][gmax - 1](args, rows_per_wg);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int STAGES>
 hipError_t tiled_instance(int64_t m, int64_t n, int64_t k, const void* aq, const float* as, const void* wq,
                           const float* ws, void* c, hipStream_t stream) {
-  constexpr int STAGES = 3;
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
   hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WM, WN, STAGES>), dim3(static_cast<unsigned>(tiles)), dim3(64 * WM * WN), 0,
                      stream, m, n, k, static_cast<const unsigned char*>(aq), as,
@@ -163,25 +163,72 @@ hipError_t tiled_instance(int64_t m, int64_t n, int64_t k, const void* aq, const
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
-                             const void* wq, const float* ws, void* c, hipStream_t stream) {
-  // 128 x 128 tiles of 4 waves while their grid fits one round of
-  // workgroups on the 256 CUs: twice the workgroups of 128 x 256 tiles,
-  // measured 1.3-1.6x faster there (every M <= 128 on the five weight
-  // shapes; up to 512-768 tokens on N = 5120..8192); a grid that would
-  // spill into a second, partly empty round is slower than the wider tiles.
-  // Otherwise 128 tokens x 256 weight rows per 8-wave workgroup (2 x 4 waves
-  // of 64 x 64).
-  const int64_t narrow_tiles = ((m + 127) / 128) * ((n + 127) / 128);
-  if (narrow_tiles <= kNumCUs) {
-    dispatch_log("gemm(tiled)", m, n, k,
-                 ("gemm_tiled_kernel BM=128 BN=128 4 waves grid=" + std::to_string(narrow_tiles)).c_str());
-    return tiled_instance<128, 128, 2, 2>(m, n, k, aq, as, wq, ws, c, stream);
+namespace {
+
+struct TileShape {
+  int bm, bn;
+  // measured time of one K step of one round of resident workgroups (all
+  // CUs busy), relative units (MI355X, Gaussian data: 1.15 / 1.5 / 1.9 us
+  // for the three 8-wave shapes)
+  int step_cost;
+  const char* desc;
+};
+constexpr TileShape kTileShapes[] = {
+    {128, 128, 0, "gemm_tiled_kernel BM=128 BN=128 4 waves 3 stages"},
+    {128, 256, 23, "gemm_tiled_kernel BM=128 BN=256 8 waves 3 stages"},
+    {192, 256, 30, "gemm_tiled_kernel BM=192 BN=256 8 waves 2 stages"},
+    {256, 256, 38, "gemm_tiled_kernel BM=256 BN=256 8 waves 2 stages"},
+};
+
+int64_t tile_count(int64_t m, int64_t n, const TileShape& t) { return ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn); }
+
+}  // namespace
+
+// Tile shape for the tiled kernel. Each workgroup fills one CU's LDS, so a
+// grid runs in ceil(tiles / 256) rounds, every round as long as its K loop.
+//  - 128 x 128 tiles of 4 waves while their grid fits one round: twice the
+//    workgroups of 128 x 256 tiles, measured 1.3-1.6x faster there (every
+//    M <= 128 on the five weight shapes; up to 512-768 tokens on
+//    N = 5120..8192);
+//  - otherwise the 8-wave shape with the least rounds x step cost. Larger
+//    tiles re-read fewer bytes per MFMA (a step of a 256 x 256 tile does
+//    twice the work of a 128 x 256 one at 1.65x its time) but make fewer
+//    tiles, so a grid just past a whole number of rounds picks the smaller
+//    tile that keeps it within them (M = 3465: (17408, 5120) takes 256 x 256,
+//    4 rounds; (5120, 8704) takes 192 x 256, 2 rounds instead of 256 x 256's
+//    1.09).
+// Ties go to the smaller tile (less padding of a ragged M).
+int tiled_shape(int64_t m, int64_t n) {
+  if (tile_count(m, n, kTileShapes[0]) <= kNumCUs) return 0;
+  int best = 1;
+  int64_t best_cost = INT64_MAX;
+  for (int i = 1; i < 4; ++i) {
+    const int64_t cost = (tile_count(m, n, kTileShapes[i]) + kNumCUs - 1) / kNumCUs * kTileShapes[i].step_cost;
+    if (cost < best_cost) {
+      best = i;
+      best_cost = cost;
+    }
   }
+  return best;
+}
+
+hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
+                             const void* wq, const float* ws, void* c, hipStream_t stream, int shape) {
+  if (shape < 0) shape = tiled_shape(m, n);
+  if (shape > 3) return hipErrorInvalidValue;
   dispatch_log("gemm(tiled)", m, n, k,
-               ("gemm_tiled_kernel BM=128 BN=256 8 waves grid=" + std::to_string(((m + 127) / 128) * ((n + 255) / 256)))
+               (std::string(kTileShapes[shape].desc) + " grid=" + std::to_string(tile_count(m, n, kTileShapes[shape])))
                    .c_str());
-  return tiled_instance<128, 256, 2, 4>(m, n, k, aq, as, wq, ws, c, stream);
+  switch (shape) {
+    case 0:
+      return tiled_instance<128, 128, 2, 2, 3>(m, n, k, aq, as, wq, ws, c, stream);
+    case 1:
+      return tiled_instance<128, 256, 2, 4, 3>(m, n, k, aq, as, wq, ws, c, stream);
+    case 2:
+      return tiled_instance<192, 256, 2, 4, 2>(m, n, k, aq, as, wq, ws, c, stream);
+    default:
+      return tiled_instance<256, 256, 2, 4, 2>(m, n, k, aq, as, wq, ws, c, stream);
+  }
 }
 
 hipError_t launch_fill_zero_bf16(int64_t count, void* c, hipStream_t stream) {

@@ -11,9 +11,11 @@
 // registers. K is walked one 128-wide scale group per step:
 //   1. the step's A slice (BM x 128 codes), W slice (BN x 128 codes) and the
 //      BM activation scales are copied global -> LDS with direct-to-LDS loads
-//      (no registers), three stages deep: steps g + 1 and g + 2 are in
-//      flight while step g computes. The scales of one group are a strided
-//      gather (one line per token), so only BM / 64 waves copy them;
+//      (no registers), STAGES deep: steps g + 1 .. g + STAGES - 1 are in
+//      flight while step g computes (three stages where they fit in the
+//      160 KB of LDS, two for the 192- and 256-token tiles). The scales of
+//      one group are a strided gather (one line per token), so only BM / 64
+//      waves copy them;
 //   2. each wave reads its W fragments once per step and streams its token
 //      fragments; one 16x16x128 FP8 MFMA per 16 x 16 sub-tile gives the
 //      group's exact products into a fresh accumulator (weight rows first
@@ -51,12 +53,24 @@ typedef __attribute__((address_space(3))) const void lds_void;
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<uintptr_t>((const lds_void*)p));
 }
-__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr(lds_base))
+// Global address = uniform 64-bit base (scalar registers) + per-lane 32-bit
+// offset, so a copy needs one vector register per lane and no 64-bit
+// address arithmetic. `sbase` must be the same in every lane; uniform()
+// states that to the compiler where it cannot prove it.
+__device__ __forceinline__ const void* uniform(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v & 0xffffffffu)));
+  const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)));
+  return reinterpret_cast<const void*>(lo | (hi << 32));
+}
+__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, void* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds_addr(lds_base))
                : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gsrc), "s"(lds_addr(lds_base))
+__device__ __forceinline__ void dma4(const void* sbase, unsigned voff, void* lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds_addr(lds_base))
                : "memory", "m0");
 }
 
@@ -205,10 +219,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
     const unsigned char* ag = a_base + g * kGroup;
     const unsigned char* wg = w_base + g * kGroup;
 #pragma unroll
-    for (int q = 0; q < A_CHUNKS; ++q) dma16(ag + a_off[q], base + 1024 * (wave + WAVES * q));
+    for (int q = 0; q < A_CHUNKS; ++q) dma16(ag, a_off[q], base + 1024 * (wave + WAVES * q));
 #pragma unroll
-    for (int q = 0; q < W_CHUNKS; ++q) dma16(wg + w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
-    if (copies_scales) dma4(sa_base + g + sa_off, base + (BM + BN) * 128 + 256 * wave);
+    for (int q = 0; q < W_CHUNKS; ++q) dma16(wg, w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
+    if (copies_scales) dma4(uniform(sa_base + g), 4 * sa_off, base + (BM + BN) * 128 + 256 * wave);
   };
 
   // Fragment read: lane's row `r` of a 128-byte-row tile, chunks quarter and

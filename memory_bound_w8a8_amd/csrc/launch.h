@@ -14,9 +14,11 @@ hipError_t launch_quant_weight(int64_t n, int64_t k, const float* w, void* wq, f
 hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                               const void* wq, const float* ws, void* c, hipStream_t stream);
 
-// LDS-tiled MFMA kernel, any m >= 1.
+// LDS-tiled MFMA kernel, any m >= 1. shape -1 picks the tile shape from
+// (m, n) (tiled_shape); 0..3 force 128x128, 128x256, 192x256, 256x256.
+int tiled_shape(int64_t m, int64_t n);
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
-                             const void* wq, const float* ws, void* c, hipStream_t stream);
+                             const void* wq, const float* ws, void* c, hipStream_t stream, int shape = -1);
 
 // The small-M entry points below serve 1 <= m <= 16 and K/128 groups within
 // the streaming instance table.

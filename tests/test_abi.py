@@ -62,6 +62,7 @@ def test_gemm_shape_errors(fp8bq):
     assert L.fp8bq_gemm(1 << 21, 1 << 21, 128, p, p, p, p, p, None) == -2  # M*N > 2^40
     assert L.fp8bq_gemm_forced(1, 129, 4, 128, p, p, p, p, p, None) == -2  # stream path serves M <= 128
     assert L.fp8bq_gemm_forced(7, 1, 4, 128, p, p, p, p, p, None) == -2  # unknown path
+    assert L.fp8bq_gemm_forced(-1, 1, 4, 128, p, p, p, p, p, None) == -2
 
 
 def test_gemm_quick_return_and_null_and_alignment(fp8bq):

@@ -41,5 +41,5 @@ def test_dispatch_log_names_each_decision_once():
     assert got["fp8bq: gemm(stream) M=32 N=17408 K=5120"].startswith("gemm_rows_kernel MT=32 act=lines")
     assert got["fp8bq: gemm(stream) M=64 N=17408 K=5120"].startswith("gemm_rows64_kernel")
     assert got["fp8bq: gemm(tiled) M=65 N=17408 K=5120"].startswith("gemm_tiled_kernel BM=128 BN=128")
-    assert got["fp8bq: gemm(tiled) M=3465 N=17408 K=5120"].startswith("gemm_tiled_kernel BM=128 BN=256")
+    assert got["fp8bq: gemm(tiled) M=3465 N=17408 K=5120"].startswith("gemm_tiled_kernel BM=256 BN=256 8 waves 2 stages grid=952")
     assert got["fp8bq: gemm_fused M=2 N=17408 K=5120"].startswith("gemm_rows_kernel MT=16 act=bf16 TOK=2")

@@ -139,6 +139,29 @@ def test_stream_and_tiled_paths_agree(m):
     assert np.max(np.abs(c_stream - c_tiled)) <= 2e-2 * rms + 2 ** -7 * np.max(np.abs(ref))
 
 
+TILE_PATHS = (fp8bq.PATH_TILED_128x128, fp8bq.PATH_TILED_128x256, fp8bq.PATH_TILED_192x256,
+              fp8bq.PATH_TILED_256x256)
+
+
+# Every tile shape of the tiled kernel, whole output against the oracle on
+# sizes with several tiles and ragged M and N tails (N not a multiple of 4
+# takes the scalar store), and bitwise equality between the shapes: each
+# output is summed group by group in the same order whatever the tiling.
+@pytest.mark.parametrize("m,n,k", [(1, 300, 128), (65, 257, 1152), (300, 1040, 640), (517, 1100, 256)])
+def test_tile_shapes_whole_output_and_bitwise(m, n, k):
+    a_q, a_s, w_q, w_s = _problem(m, n, k)
+    ref = gemm_ref(a_q, a_s, w_q, w_s)
+    args = [to_gpu(a_q), to_gpu(a_s), to_gpu(w_q), to_gpu(w_s)]
+    outs = []
+    for path in TILE_PATHS:
+        c = fp8bq.gemm_forced(path, *args)
+        torch.cuda.synchronize()
+        assert_gemm_close(bf16_to_f64(c), ref, what=f"tile path {path} M={m} N={n} K={k}")
+        outs.append(c)
+    for path, c in zip(TILE_PATHS[1:], outs[1:]):
+        assert torch.equal(c.view(torch.int16), outs[0].view(torch.int16)), f"tile path {path}"
+
+
 def test_deterministic_repeat_calls():
     a_q, a_s, w_q, w_s = _problem(8, 5120, 3072)
     args = [to_gpu(a_q), to_gpu(a_s), to_gpu(w_q), to_gpu(w_s)]
@@ -230,3 +253,18 @@ def test_full_size_sampled_outputs(m, n, k, weights_on_gpu):
     ref = gemm_ref_at(oa_q, oa_s, wq_cat, ws_cat, rr.ravel(), col_local[cc.ravel()])
     got = bf16_to_f64(c[rows][:, torch.from_numpy(col_global).to(c.device)]).ravel()
     assert_gemm_close(got, ref, what=f"M={m} N={n} K={k}")
+
+
+# The prefill size on both prefill shapes: the tile shape gemm() picks
+# (256 x 256 and 192 x 256 tiles there), whose sampled outputs are checked
+# against the oracle above, is bitwise equal to every other tile shape.
+@pytest.mark.parametrize("n,k", workloads.PREFILL_SHAPES)
+def test_prefill_tile_shapes_bitwise(n, k, weights_on_gpu):
+    w_q, w_s = weights_on_gpu(n, k)
+    m = workloads.PREFILL_M
+    a_q, a_s = fp8bq.quant_act(to_gpu(workloads.activation(m, n, k)))
+    c = fp8bq.gemm(a_q, a_s, w_q, w_s)
+    for path in TILE_PATHS:
+        c_path = fp8bq.gemm_forced(path, a_q, a_s, w_q, w_s)
+        torch.cuda.synchronize()
+        assert torch.equal(c_path.view(torch.int16), c.view(torch.int16)), f"tile path {path}"
