@@ -371,6 +371,68 @@ def m_sweep():
     return rows
 
 
+def ceilings():
+    """What this GPU delivers, to read the roofline fractions against besides
+    the published peaks (the library's measurement kernels). Each figure is
+    a run of back-to-back launches captured in a HIP graph and replayed, so
+    that the host's launch rate (several microseconds per call through
+    Python) does not bound it:
+    - the streaming-read time of each transfer size the GEMM moves per call
+      (the five shapes' bytes at M = 1, the vocabulary projection, 1 GiB):
+      256 workgroups of 512 threads, buffers rotating over >= 1 GiB;
+    - one empty launch of the decode kernels' grid (256 x 512): the fixed
+      cost each call pays;
+    - the FP8 16x16x128 MFMA rate of 1024 workgroups x 4 waves x 8
+      independent chains (the matrix-core peak at the clock this load runs).
+    The median of three replays is reported."""
+    dev = torch.device("cuda:0")
+
+    def graph_us(launch, count):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(count):
+                launch(i)
+        g.replay()
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            e1.synchronize()
+            runs.append(e0.elapsed_time(e1) * 1e3 / count)
+        del g
+        return sorted(runs)[1]
+
+    sizes = [(f"({n}, {k}) at M=1", gemm_bytes(1, n, k)) for n, k in workloads.SHAPES]
+    sizes += [("vocabulary projection (152064, 5120)", 152064 * 5120), ("1 GiB", 1 << 30)]
+    pool = torch.empty(3 << 30, dtype=torch.uint8, device=dev)
+    pool.random_(0, 256)
+    sink = torch.empty(256, dtype=torch.int32, device=dev)
+    read = []
+    for name, nbytes in sizes:
+        nbytes = nbytes // 256 * 256
+        copies = max(2, min(pool.numel() // nbytes, -(-(1 << 30) // nbytes) + 1))
+        views = [pool[i * nbytes:(i + 1) * nbytes] for i in range(copies)]
+        us = graph_us(lambda i: fp8bq.mb_read(views[i % copies], 256, sink), max(24, 2 * copies))
+        read.append({"what": name, "bytes": nbytes, "us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+                     "pct_of_8TBps": round(nbytes / us / 1e3 / 80, 1)})
+        print(f"bench: read {name} {nbytes} B: {us:.2f} us", file=sys.stderr, flush=True)
+    del pool, views
+    torch.cuda.empty_cache()
+    empty_us = graph_us(lambda i: fp8bq.mb_empty(256, 512), 500)
+    print(f"bench: empty launch {empty_us:.3f} us", file=sys.stderr, flush=True)
+    grid, iters = 1024, 4096
+    msink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    mfma_us = graph_us(lambda i: fp8bq.mb_mfma(grid, iters, sink=msink), 3)
+    flops = grid * 4 * 8 * iters * 2.0 * 16 * 16 * 128
+    return {"read": read, "empty_launch_us": round(empty_us, 3),
+            "mfma_e4m3_16x16x128": {"TFLOPs": round(flops / mfma_us / 1e6, 1), "us": round(mfma_us, 1),
+                                    "frac_of_5000": round(flops / mfma_us / 1e6 / FP8_PEAK_TFLOPS, 4)}}
+
+
 def cpu_baseline(budget_s=20.0, rows=4096):
     """The CPU oracle (numpy, fp64 GEMM) on a bounded sample: quantise the
     activation and compute the GEMM for M = 1..8 against the first `rows`
@@ -420,6 +482,9 @@ def main():
                     help="run only this leg and print its JSON line (for profiling one kernel family)")
     ap.add_argument("--m-sweep", action="store_true",
                     help="instead of the benchmark, time fp8bq_gemm over an M grid on the five shapes (one JSON line)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the benchmark, measure the streaming-read, launch and FP8 MFMA ceilings "
+                         "(one JSON line)")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a dispatch of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -441,6 +506,11 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"metric": "prefill block-FP8 GEMM us/call", "data": "synthetic",
                           "prefill": prefill(Plan(1)), "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
+
+    if args.ceilings:
+        print(json.dumps({"metric": "measured ceilings", "data": "synthetic", **ceilings(),
+                          "device": torch.cuda.get_device_name(0)}), flush=True)
         return
 
     if args.m_sweep:

@@ -248,6 +248,34 @@ int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void *h
                        int32_t *pick_out, void *stream);
 
 /* Human-readable name of a status code; never NULL. */
+/*
+ * Measurement kernels: what this machine delivers, to read the GEMM's
+ * roofline fractions against besides the published peaks (page 1, SmartX
+ * blog: "single-stream optimisation" reports bytes per decode step over time
+ * against a calibrated bandwidth; "test background" calibrates the tools
+ * first). All three only read their inputs and write `sink`.
+ *
+ * fp8bq_mb_read: streaming read of `bytes` bytes at `buf` (bytes % 16 == 0,
+ *   buf 16-B aligned) by `grid` (1..65536) workgroups of 512 threads,
+ *   consecutive lanes on consecutive 16-byte units, non-temporal loads,
+ *   four in flight per lane. sink [grid] uint32 (out): the XOR of the
+ *   32-bit words each workgroup read; XORed together they equal the XOR of
+ *   every word of the buffer. bytes == 0 (buf may then be NULL) writes
+ *   zeros.
+ * fp8bq_mb_empty: one launch of an empty kernel, `grid` (1..2^20)
+ *   workgroups of `block` (64..1024, a multiple of 64) threads.
+ * fp8bq_mb_mfma_e4m3: `grid` (1..65536) workgroups of 4 waves, each wave
+ *   8 independent chains of `iters` (0..2^24) V_MFMA_F32_16X16X128_F8F6F4
+ *   (2 * 16 * 16 * 128 flop each) with every operand byte the e4m3 code
+ *   `code` (0..255, not a NaN code). sink [grid * 256] fp32 (out): thread t
+ *   writes 4096 * iters * decode(code)^2 (exact while that fits in fp32's
+ *   24 bits).
+ * Errors as for the GEMM: FP8BQ_ERR_SHAPE, _NULL, _ALIGN, _DEVICE, _LAUNCH.
+ */
+int fp8bq_mb_read(const void *buf, int64_t bytes, int grid, unsigned *sink, void *stream);
+int fp8bq_mb_empty(int grid, int block, void *stream);
+int fp8bq_mb_mfma_e4m3(int grid, int iters, int code, float *sink, void *stream);
+
 const char *fp8bq_status_string(int status);
 
 #ifdef __cplusplus

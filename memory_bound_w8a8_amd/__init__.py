@@ -41,6 +41,9 @@ EXPORTS = (
     "fp8bq_topk_workspace_bytes",
     "fp8bq_topk_bf16",
     "fp8bq_rescore_bf16",
+    "fp8bq_mb_read",
+    "fp8bq_mb_empty",
+    "fp8bq_mb_mfma_e4m3",
     "fp8bq_status_string",
 )
 
@@ -75,10 +78,15 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_topk_workspace_bytes.restype = i64
         L.fp8bq_topk_bf16.argtypes = [i64, i64, i64, vp, vp, i64, vp, vp, vp]
         L.fp8bq_rescore_bf16.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        ci = ctypes.c_int
+        L.fp8bq_mb_read.argtypes = [vp, i64, ci, vp, vp]
+        L.fp8bq_mb_empty.argtypes = [ci, ci, vp]
+        L.fp8bq_mb_mfma_e4m3.argtypes = [ci, ci, ci, vp, vp]
         L.fp8bq_status_string.argtypes = [ctypes.c_int]
         L.fp8bq_status_string.restype = ctypes.c_char_p
         for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path",
-                     "fp8bq_gemm_w8a16", "fp8bq_gemm_fused", "fp8bq_topk_bf16", "fp8bq_rescore_bf16"):
+                     "fp8bq_gemm_w8a16", "fp8bq_gemm_fused", "fp8bq_topk_bf16", "fp8bq_rescore_bf16",
+                     "fp8bq_mb_read", "fp8bq_mb_empty", "fp8bq_mb_mfma_e4m3"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -288,3 +296,34 @@ def two_stage(h: torch.Tensor, w_q, w_s, w_bf16: torch.Tensor, k: int, workspace
     idx, _ = topk(logits, k, workspace)
     scores, pick = rescore(h, w_bf16, idx)
     return pick, idx, scores
+
+
+# Measurement kernels (the machine's own ceilings for the roofline figures).
+
+def mb_read(buf: torch.Tensor, grid: int = 256, sink: torch.Tensor = None) -> torch.Tensor:
+    """Streaming read of a contiguous GPU buffer (size a multiple of 16
+    bytes); returns the per-workgroup XOR words (uint32 viewed as int32)."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("mb_read: buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(grid, dtype=torch.int32, device=buf.device)
+    _check("fp8bq_mb_read", lib().fp8bq_mb_read(_ptr(buf), nbytes, int(grid), _ptr(sink), _stream(buf)))
+    return sink
+
+
+def mb_empty(grid: int, block: int, device=None) -> None:
+    """One launch of an empty kernel on the current stream."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    _check("fp8bq_mb_empty", lib().fp8bq_mb_empty(int(grid), int(block), torch.cuda.current_stream(dev).cuda_stream))
+
+
+def mb_mfma(grid: int, iters: int, code: int = 0x38, sink: torch.Tensor = None, device=None) -> torch.Tensor:
+    """grid x 4 waves x 8 x iters FP8 16x16x128 MFMAs; returns the per-thread
+    sums (fp32 [grid * 256], each 4096 * iters * decode(code)^2)."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    if sink is None:
+        sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    _check("fp8bq_mb_mfma_e4m3",
+           lib().fp8bq_mb_mfma_e4m3(int(grid), int(iters), int(code), _ptr(sink), torch.cuda.current_stream(dev).cuda_stream))
+    return sink

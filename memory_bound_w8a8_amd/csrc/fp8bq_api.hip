@@ -231,4 +231,32 @@ const char* fp8bq_status_string(int status) {
   }
 }
 
+int fp8bq_mb_read(const void* buf, int64_t bytes, int grid, unsigned* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0 || grid < 1 || grid > 65536) return FP8BQ_ERR_SHAPE;
+  if ((buf == nullptr && bytes != 0) || sink == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return FP8BQ_ERR_ALIGN;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(fp8bq::launch_mb_read(buf, bytes, grid, sink, static_cast<hipStream_t>(stream)));
+}
+
+int fp8bq_mb_empty(int grid, int block, void* stream) {
+  if (grid < 1 || grid > (1 << 20) || block < 64 || block > 1024 || block % 64 != 0) return FP8BQ_ERR_SHAPE;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(fp8bq::launch_mb_empty(grid, block, static_cast<hipStream_t>(stream)));
+}
+
+int fp8bq_mb_mfma_e4m3(int grid, int iters, int code, float* sink, void* stream) {
+  if (grid < 1 || grid > 65536 || iters < 0 || iters > (1 << 24) || code < 0 || code > 255 ||
+      (code & 0x7f) == 0x7f)
+    return FP8BQ_ERR_SHAPE;
+  if (sink == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(sink, 4)) return FP8BQ_ERR_ALIGN;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(
+      fp8bq::launch_mb_mfma(grid, iters, static_cast<unsigned>(code), sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

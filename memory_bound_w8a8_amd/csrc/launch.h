@@ -47,6 +47,15 @@ hipError_t launch_rescore(int64_t m, int64_t kdim, int64_t v, int64_t k, const v
 // -> kernel description once to stderr; a no-op otherwise.
 void dispatch_log(const char* entry, int64_t m, int64_t n, int64_t k, const char* kernel);
 
+// Measurement kernels (microbench.hip): streaming read of `bytes` (a
+// multiple of 16) with `grid` workgroups of 512 threads, one XOR word per
+// workgroup into sink[grid]; an empty kernel; `grid` workgroups of 4 waves
+// each running 8 x iters FP8 MFMAs on the e4m3 code `code`, one float per
+// thread into sink[grid * 256].
+hipError_t launch_mb_read(const void* buf, int64_t bytes, int grid, unsigned* sink, hipStream_t stream);
+hipError_t launch_mb_empty(int grid, int block, hipStream_t stream);
+hipError_t launch_mb_mfma(int grid, int iters, unsigned code, float* sink, hipStream_t stream);
+
 // C = 0 (used for K == 0).
 hipError_t launch_fill_zero_bf16(int64_t count, void* c, hipStream_t stream);
 

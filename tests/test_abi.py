@@ -31,7 +31,8 @@ def _declared():
 def test_header_declares_the_abi():
     assert _declared() == {"fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_path",
                            "fp8bq_gemm_forced", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16", "fp8bq_topk_workspace_bytes",
-                           "fp8bq_topk_bf16", "fp8bq_rescore_bf16", "fp8bq_status_string"}
+                           "fp8bq_topk_bf16", "fp8bq_rescore_bf16", "fp8bq_mb_read", "fp8bq_mb_empty",
+                           "fp8bq_mb_mfma_e4m3", "fp8bq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(fp8bq):
@@ -230,3 +231,25 @@ def test_binding_rejects_cpu_tensors(fp8bq):
     with pytest.raises(ValueError):
         fp8bq.gemm(torch.zeros(1, 128, dtype=torch.uint8), torch.zeros(1, 1), torch.zeros(4, 128, dtype=torch.uint8),
                    torch.zeros(1, 1))
+
+
+def test_measurement_kernel_argument_errors(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    assert L.fp8bq_mb_read(p, 24, 256, p, None) == -2  # bytes % 16
+    assert L.fp8bq_mb_read(p, -16, 256, p, None) == -2
+    assert L.fp8bq_mb_read(p, 16, 0, p, None) == -2  # grid
+    assert L.fp8bq_mb_read(p, 16, 65537, p, None) == -2
+    assert L.fp8bq_mb_read(None, 16, 256, p, None) == -1  # NULL allowed only for bytes == 0
+    assert L.fp8bq_mb_read(p, 16, 256, None, None) == -1
+    assert L.fp8bq_mb_read(p + 8, 16, 256, p, None) == -3
+    assert L.fp8bq_mb_empty(0, 64, None) == -2
+    assert L.fp8bq_mb_empty(1, 100, None) == -2  # block not a multiple of 64
+    assert L.fp8bq_mb_empty(1, 2048, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3(0, 1, 0x38, p, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3(1, -1, 0x38, p, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3(1, 1, 0x7F, p, None) == -2  # NaN code
+    assert L.fp8bq_mb_mfma_e4m3(1, 1, 0xFF, p, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3(1, 1, 256, p, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3(1, 1, 0x38, None, None) == -1
+    assert L.fp8bq_mb_mfma_e4m3(1, 1, 0x38, p + 2, None) == -3
