@@ -23,6 +23,12 @@ for m in (1, 3, 1, 16, 32, 64, 65, 3465):
     a_q, a_s = fp8bq.quant_act(torch.randn(m, k, device=dev).to(torch.bfloat16))
     fp8bq.gemm(a_q, a_s, w_q, w_s)
 fp8bq.gemm_fused(torch.randn(2, k, device=dev).to(torch.bfloat16), w_q, w_s)
+# tile shapes by rounds x step cost on (5120, 8704): 192 x 256 at the prefill size,
+# 128 x 256 where it keeps the grid within the same rounds
+w_q, w_s = fp8bq.quant_weight(torch.randn(5120, 8704, device=dev) * 0.02)
+for m in (3465, 1024):
+    a_q, a_s = fp8bq.quant_act(torch.randn(m, 8704, device=dev).to(torch.bfloat16))
+    fp8bq.gemm(a_q, a_s, w_q, w_s)
 torch.cuda.synchronize()
 """
 
@@ -43,3 +49,7 @@ def test_dispatch_log_names_each_decision_once():
     assert got["fp8bq: gemm(tiled) M=65 N=17408 K=5120"].startswith("gemm_tiled_kernel BM=128 BN=128")
     assert got["fp8bq: gemm(tiled) M=3465 N=17408 K=5120"].startswith("gemm_tiled_kernel BM=256 BN=256 8 waves 2 stages grid=952")
     assert got["fp8bq: gemm_fused M=2 N=17408 K=5120"].startswith("gemm_rows_kernel MT=16 act=bf16 TOK=2")
+    # 380 tiles of 192 x 256 (2 rounds) beat 280 of 256 x 256 (1.09 rounds) and 560 of 128 x 256 (2.19)
+    assert got["fp8bq: gemm(tiled) M=3465 N=5120 K=8704"] == "gemm_tiled_kernel BM=192 BN=256 8 waves 2 stages grid=380"
+    # 160 tiles of 128 x 256 fit one round; the larger tiles cost more per step
+    assert got["fp8bq: gemm(tiled) M=1024 N=5120 K=8704"] == "gemm_tiled_kernel BM=128 BN=256 8 waves 3 stages grid=160"
