@@ -95,11 +95,10 @@ int fp8bq_quant_weight(int64_t N, int64_t K, const float *W_f32, void *W_fp8, fl
  *   W_fp8    [N, K] uint8 codes,  W_scales [ceil(N/128), K/128] fp32 (read)
  *   C_bf16   [M, N] bf16, written, fp32 accumulation rounded to bf16 RNE.
  * Every M >= 1 is served by a kernel chosen from explicit ranges (no
- * nearest-size table): M <= 64 streams the weights once; 65 <= M <= 128
- * streams them twice (tokens 0..63, then the rest) when N <= 16256 (where
- * the tiled kernel's grid of ceil(N / 128) workgroups would fill under half
- * the 256 CUs); the LDS-tiled MFMA kernel otherwise. The summation order
- * differs from the fp64
+ * nearest-size table): M <= 64 streams the weights once; M > 64 runs the
+ * LDS-tiled MFMA kernel, whose tile shape (64x64 up to 256x256 tokens x
+ * weight rows) follows from (M, N) by the number of rounds of workgroups
+ * its grid needs on the 256 CUs. The summation order differs from the fp64
  * definition; results agree within fp32 accumulation plus bf16 rounding.
  * Two identical calls give bitwise-identical C (no atomics).
  * K == 0 writes zeros. Errors: NULL pointer; negative size; K % 128 != 0;
@@ -123,7 +122,10 @@ enum {
   FP8BQ_PATH_TILED_128x128 = 3,
   FP8BQ_PATH_TILED_128x256 = 4,
   FP8BQ_PATH_TILED_192x256 = 5,
-  FP8BQ_PATH_TILED_256x256 = 6
+  FP8BQ_PATH_TILED_256x256 = 6,
+  FP8BQ_PATH_TILED_64x128 = 7,
+  FP8BQ_PATH_TILED_128x64 = 8,
+  FP8BQ_PATH_TILED_64x64 = 9
 };
 int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K);
 

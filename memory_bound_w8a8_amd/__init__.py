@@ -27,6 +27,7 @@ FP8BQ_OK = 0
 PATH_NONE, PATH_STREAM, PATH_TILED = 0, 1, 2
 # tile shapes of the tiled kernel (tokens x weight rows), for gemm_forced
 PATH_TILED_128x128, PATH_TILED_128x256, PATH_TILED_192x256, PATH_TILED_256x256 = 3, 4, 5, 6
+PATH_TILED_64x128, PATH_TILED_128x64, PATH_TILED_64x64 = 7, 8, 9
 PATH_NAMES = {PATH_NONE: "none", PATH_STREAM: "stream", PATH_TILED: "tiled"}
 
 # Every symbol the C ABI exports (kept in step with include/fp8bq.h).

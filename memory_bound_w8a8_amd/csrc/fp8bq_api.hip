@@ -12,8 +12,7 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // bound on M*K, N*K, M*N
 constexpr int64_t kStreamMaxM = 64;              // streaming kernels serve 1..64 tokens per launch
-constexpr int64_t kStreamSplitMaxM = 128;        // ... and 65..128 as two launches (64 + the rest)
-constexpr int64_t kStreamSplitMaxTiles = 128;    // ... where the tiled kernel would fill under half the CUs
+constexpr int64_t kStreamSplitMaxM = 128;        // forced streaming path: 65..128 as two launches (64 + the rest)
 constexpr int64_t kTiledMaxK = int64_t(1) << 24; // tiled kernel: 32-bit offsets within a 256-row tile
 constexpr int kMaxDevices = 64;
 constexpr int64_t kSmallMaxM = 16;               // fused and weight-only paths: one 16-token tile
@@ -60,13 +59,12 @@ int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A_fp8, const fl
   return FP8BQ_OK;
 }
 
-// 1..64 tokens stream the weights once; 65..128 tokens also stream (twice:
-// tokens 0..63, then the rest) when the tiled kernel's grid, one workgroup
-// per 128 weight rows at this M, would leave more than half the CUs idle;
-// otherwise, and beyond 128 tokens, the tiled kernel.
-int gemm_path(int64_t M, int64_t N) {
+// 1..64 tokens stream the weights once; beyond, the tiled kernel, whose
+// 4-wave 64 x 64 to 128 x 128 tiles keep the CUs filled at 65..128 tokens
+// (streaming the weights twice, tokens 0..63 and then the rest, measured
+// 15-30% slower on the N = 5120..8192 shapes and 15% on N = 17408).
+int gemm_path(int64_t M) {
   if (M <= kStreamMaxM) return FP8BQ_PATH_STREAM;
-  if (M <= kStreamSplitMaxM && (N + 127) / 128 < kStreamSplitMaxTiles) return FP8BQ_PATH_STREAM;
   return FP8BQ_PATH_TILED;
 }
 
@@ -84,7 +82,7 @@ int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const
              const void* W_fp8, const float* W_scales, void* C_bf16, void* stream) {
   int st = check_gemm_args(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16);
   if (st != FP8BQ_OK) return st;
-  const bool tiled = path == FP8BQ_PATH_TILED || (path >= FP8BQ_PATH_TILED_128x128 && path <= FP8BQ_PATH_TILED_256x256);
+  const bool tiled = path == FP8BQ_PATH_TILED || (path >= FP8BQ_PATH_TILED_128x128 && path <= FP8BQ_PATH_TILED_64x64);
   if (path == FP8BQ_PATH_STREAM && M > kStreamSplitMaxM) return FP8BQ_ERR_SHAPE;
   if (tiled && K >= kTiledMaxK) return FP8BQ_ERR_SHAPE;
   if (path != FP8BQ_PATH_STREAM && !tiled) return FP8BQ_ERR_SHAPE;
@@ -127,7 +125,7 @@ int fp8bq_quant_weight(int64_t N, int64_t K, const float* W_f32, void* W_fp8, fl
 int fp8bq_gemm(int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales, const void* W_fp8,
                const float* W_scales, void* C_bf16, void* stream) {
   if (M < 0 || N < 0) return FP8BQ_ERR_SHAPE;
-  return run_gemm(gemm_path(M, N), M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
+  return run_gemm(gemm_path(M), M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
 }
 
 int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales,
@@ -139,7 +137,7 @@ int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
   if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_PATH_NONE;
-  return gemm_path(M, N);
+  return gemm_path(M);
 }
 
 int fp8bq_gemm_fused(int64_t M, int64_t N, int64_t K, const void* A_bf16, const void* W_fp8, const float* W_scales,

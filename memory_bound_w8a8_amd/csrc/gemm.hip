@@ -167,46 +167,64 @@ namespace {
 
 struct TileShape {
   int bm, bn;
-  // measured time of one K step of one round of resident workgroups (all
-  // CUs busy), relative units (MI355X, Gaussian data: 1.15 / 1.5 / 1.9 us
-  // for the three 8-wave shapes)
-  int step_cost;
+  int per_cu;  // workgroups one CU holds at once (LDS: 1 for 8-wave and 128 x 128 tiles, 2 for the halves, 3 for 64 x 64)
+  // measured time of one K step of one round of resident workgroups,
+  // 1/100 us (MI355X, Gaussian data): with at most one workgroup per CU,
+  // and with two or three on some CUs (per_cu > 1, grids of more than 256
+  // tiles)
+  int step_cost, step_cost2;
   const char* desc;
 };
+// Indexed as the forced tile-shape paths of fp8bq_gemm_forced (0..6 =
+// FP8BQ_PATH_TILED_128x128 .. FP8BQ_PATH_TILED_64x64).
 constexpr TileShape kTileShapes[] = {
-    {128, 128, 0, "gemm_tiled_kernel BM=128 BN=128 4 waves 3 stages"},
-    {128, 256, 23, "gemm_tiled_kernel BM=128 BN=256 8 waves 3 stages"},
-    {192, 256, 30, "gemm_tiled_kernel BM=192 BN=256 8 waves 2 stages"},
-    {256, 256, 38, "gemm_tiled_kernel BM=256 BN=256 8 waves 2 stages"},
+    {128, 128, 1, 85, 85, "gemm_tiled_kernel BM=128 BN=128 4 waves 3 stages"},
+    {128, 256, 1, 115, 115, "gemm_tiled_kernel BM=128 BN=256 8 waves 3 stages"},
+    {192, 256, 1, 150, 150, "gemm_tiled_kernel BM=192 BN=256 8 waves 2 stages"},
+    {256, 256, 1, 190, 190, "gemm_tiled_kernel BM=256 BN=256 8 waves 2 stages"},
+    {64, 128, 2, 60, 100, "gemm_tiled_kernel BM=64 BN=128 4 waves 3 stages"},
+    {128, 64, 2, 60, 100, "gemm_tiled_kernel BM=128 BN=64 4 waves 3 stages"},
+    {64, 64, 3, 52, 90, "gemm_tiled_kernel BM=64 BN=64 4 waves 3 stages"},
 };
+constexpr int kNumTileShapes = sizeof(kTileShapes) / sizeof(kTileShapes[0]);
 
 int64_t tile_count(int64_t m, int64_t n, const TileShape& t) { return ((m + t.bm - 1) / t.bm) * ((n + t.bn - 1) / t.bn); }
 
 }  // namespace
 
-// Tile shape for the tiled kernel. Each workgroup fills one CU's LDS, so a
-// grid runs in ceil(tiles / 256) rounds, every round as long as its K loop.
-//  - 128 x 128 tiles of 4 waves while their grid fits one round: twice the
-//    workgroups of 128 x 256 tiles, measured 1.3-1.6x faster there (every
-//    M <= 128 on the five weight shapes; up to 512-768 tokens on
-//    N = 5120..8192);
-//  - otherwise the 8-wave shape with the least rounds x step cost. Larger
-//    tiles re-read fewer bytes per MFMA (a step of a 256 x 256 tile does
-//    twice the work of a 128 x 256 one at 1.65x its time) but make fewer
-//    tiles, so a grid just past a whole number of rounds picks the smaller
-//    tile that keeps it within them (M = 3465: (17408, 5120) takes 256 x 256,
-//    4 rounds; (5120, 8704) takes 192 x 256, 2 rounds instead of 256 x 256's
-//    1.09).
-// Ties go to the smaller tile (less padding of a ragged M).
+// Tile shape for the tiled kernel: the one with the least rounds x step
+// cost. A grid runs in ceil(tiles / (256 x workgroups per CU)) rounds, each
+// as long as its K loop; the step costs are measured.
+//  - Larger tiles re-read fewer LDS and L2 bytes per MFMA (a step of a
+//    256 x 256 tile does twice the work of a 128 x 256 one at 1.65x its
+//    time) but make fewer tiles, so a grid just past a whole number of
+//    rounds takes the smaller tile that stays within them (M = 3465:
+//    (17408, 5120) takes 256 x 256, 4 rounds; (5120, 8704) 192 x 256, 2
+//    rounds instead of 256 x 256's 1.09).
+//  - Few tokens leave most CUs idle with large tiles: the 4-wave halves
+//    (64 x 128, 128 x 64; two fit in one CU's LDS) and quarters (64 x 64,
+//    three per CU) fill them, e.g. 160 tiles instead of 40 at M = 65..128
+//    on N = 5120 (M = 128 at (5120, 8704): 32 us against 59 with 128 x 128
+//    tiles and 48 streaming the weights twice). Once their grid outgrows
+//    one workgroup per CU the smaller tiles lose their edge (64 x 64 at
+//    M = 192 on N = 8192: 35 us against 26 for 128 x 64).
+// Equal costs go to the grid with more tiles (the better-filled machine),
+// then to the earlier shape in the order 64x64, 64x128, 128x64, 128x128,
+// 128x256, 192x256, 256x256.
 int tiled_shape(int64_t m, int64_t n) {
-  if (tile_count(m, n, kTileShapes[0]) <= kNumCUs) return 0;
-  int best = 1;
-  int64_t best_cost = INT64_MAX;
-  for (int i = 1; i < 4; ++i) {
-    const int64_t cost = (tile_count(m, n, kTileShapes[i]) + kNumCUs - 1) / kNumCUs * kTileShapes[i].step_cost;
-    if (cost < best_cost) {
+  constexpr int kOrder[kNumTileShapes] = {6, 4, 5, 0, 1, 2, 3};
+  int best = 0;
+  int64_t best_cost = INT64_MAX, best_tiles = 0;
+  for (int i : kOrder) {
+    const TileShape& t = kTileShapes[i];
+    const int64_t tiles = tile_count(m, n, t);
+    const int64_t cap = static_cast<int64_t>(kNumCUs) * t.per_cu;
+    const int64_t rounds = (tiles + cap - 1) / cap;
+    const int64_t cost = rounds * (tiles > kNumCUs ? t.step_cost2 : t.step_cost);
+    if (cost < best_cost || (cost == best_cost && tiles > best_tiles)) {
       best = i;
       best_cost = cost;
+      best_tiles = tiles;
     }
   }
   return best;
@@ -215,7 +233,7 @@ int tiled_shape(int64_t m, int64_t n) {
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                              const void* wq, const float* ws, void* c, hipStream_t stream, int shape) {
   if (shape < 0) shape = tiled_shape(m, n);
-  if (shape > 3) return hipErrorInvalidValue;
+  if (shape >= kNumTileShapes) return hipErrorInvalidValue;
   dispatch_log("gemm(tiled)", m, n, k,
                (std::string(kTileShapes[shape].desc) + " grid=" + std::to_string(tile_count(m, n, kTileShapes[shape])))
                    .c_str());
@@ -226,8 +244,14 @@ hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, co
       return tiled_instance<128, 256, 2, 4, 3>(m, n, k, aq, as, wq, ws, c, stream);
     case 2:
       return tiled_instance<192, 256, 2, 4, 2>(m, n, k, aq, as, wq, ws, c, stream);
-    default:
+    case 3:
       return tiled_instance<256, 256, 2, 4, 2>(m, n, k, aq, as, wq, ws, c, stream);
+    case 4:
+      return tiled_instance<64, 128, 1, 4, 3>(m, n, k, aq, as, wq, ws, c, stream);
+    case 5:
+      return tiled_instance<128, 64, 2, 2, 3>(m, n, k, aq, as, wq, ws, c, stream);
+    default:
+      return tiled_instance<64, 64, 2, 2, 3>(m, n, k, aq, as, wq, ws, c, stream);
   }
 }
 

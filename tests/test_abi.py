@@ -62,7 +62,7 @@ def test_gemm_shape_errors(fp8bq):
     assert L.fp8bq_gemm(1, 4, 100, p, p, p, p, p, None) == -2
     assert L.fp8bq_gemm(1 << 21, 1 << 21, 128, p, p, p, p, p, None) == -2  # M*N > 2^40
     assert L.fp8bq_gemm_forced(1, 129, 4, 128, p, p, p, p, p, None) == -2  # stream path serves M <= 128
-    assert L.fp8bq_gemm_forced(7, 1, 4, 128, p, p, p, p, p, None) == -2  # unknown path
+    assert L.fp8bq_gemm_forced(10, 1, 4, 128, p, p, p, p, p, None) == -2  # unknown path
     assert L.fp8bq_gemm_forced(-1, 1, 4, 128, p, p, p, p, p, None) == -2
 
 
@@ -201,13 +201,10 @@ def test_gemm_path_dispatch_by_explicit_m_ranges(fp8bq):
         assert L.fp8bq_gemm_path(m, 17408, 5120) == fp8bq.PATH_STREAM, m
     for m in (65, 128, 2048, 3465, 4096):
         assert L.fp8bq_gemm_path(m, 17408, 5120) == fp8bq.PATH_TILED, m
-    # 65..128 tokens stream twice where the tiled grid (ceil(N / 128)
-    # workgroups) would fill under half the CUs
-    for n in (5120, 7168, 8192, 16256):
-        for m in (65, 100, 128):
-            assert L.fp8bq_gemm_path(m, n, 5120) == fp8bq.PATH_STREAM, (m, n)
-        assert L.fp8bq_gemm_path(129, n, 5120) == fp8bq.PATH_TILED, n
-    assert L.fp8bq_gemm_path(65, 16257, 5120) == fp8bq.PATH_TILED
+    # beyond 64 tokens the tiled kernel on every weight shape
+    for n in (128, 5120, 7168, 8192, 16256):
+        for m in (65, 100, 128, 129):
+            assert L.fp8bq_gemm_path(m, n, 5120) == fp8bq.PATH_TILED, (m, n)
     assert L.fp8bq_gemm_path(1, 17408, 5000) == -2
 
 

@@ -26,7 +26,7 @@ fp8bq.gemm_fused(torch.randn(2, k, device=dev).to(torch.bfloat16), w_q, w_s)
 # tile shapes by rounds x step cost on (5120, 8704): 192 x 256 at the prefill size,
 # 128 x 256 where it keeps the grid within the same rounds
 w_q, w_s = fp8bq.quant_weight(torch.randn(5120, 8704, device=dev) * 0.02)
-for m in (3465, 1024):
+for m in (3465, 1024, 128, 192, 256):
     a_q, a_s = fp8bq.quant_act(torch.randn(m, 8704, device=dev).to(torch.bfloat16))
     fp8bq.gemm(a_q, a_s, w_q, w_s)
 torch.cuda.synchronize()
@@ -53,3 +53,9 @@ def test_dispatch_log_names_each_decision_once():
     assert got["fp8bq: gemm(tiled) M=3465 N=5120 K=8704"] == "gemm_tiled_kernel BM=192 BN=256 8 waves 2 stages grid=380"
     # 160 tiles of 128 x 256 fit one round; the larger tiles cost more per step
     assert got["fp8bq: gemm(tiled) M=1024 N=5120 K=8704"] == "gemm_tiled_kernel BM=128 BN=256 8 waves 3 stages grid=160"
+    # few tokens on a narrow weight: 64 x 64 tiles fill the CUs while their
+    # grid fits one round (160 at M = 128, 240 at 192); at 256 tokens (320)
+    # the 4-wave halves do (160 tiles of 64 x 128, the first of the two in order)
+    assert got["fp8bq: gemm(tiled) M=128 N=5120 K=8704"] == "gemm_tiled_kernel BM=64 BN=64 4 waves 3 stages grid=160"
+    assert got["fp8bq: gemm(tiled) M=192 N=5120 K=8704"] == "gemm_tiled_kernel BM=64 BN=64 4 waves 3 stages grid=240"
+    assert got["fp8bq: gemm(tiled) M=256 N=5120 K=8704"] == "gemm_tiled_kernel BM=64 BN=128 4 waves 3 stages grid=160"

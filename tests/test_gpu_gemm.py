@@ -140,7 +140,8 @@ def test_stream_and_tiled_paths_agree(m):
 
 
 TILE_PATHS = (fp8bq.PATH_TILED_128x128, fp8bq.PATH_TILED_128x256, fp8bq.PATH_TILED_192x256,
-              fp8bq.PATH_TILED_256x256)
+              fp8bq.PATH_TILED_256x256, fp8bq.PATH_TILED_64x128, fp8bq.PATH_TILED_128x64,
+              fp8bq.PATH_TILED_64x64)
 
 
 # Every tile shape of the tiled kernel, whole output against the oracle on
