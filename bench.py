@@ -362,7 +362,10 @@ def m_sweep():
             e1.record(stream)
             e1.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / reps
-            rows.append({"N": n, "K": k, "M": m, "path": fp8bq.PATH_NAMES[L.fp8bq_gemm_path(m, n, k)],
+            path = L.fp8bq_gemm_path(m, n, k)
+            if path == fp8bq.PATH_TILED:
+                path = L.fp8bq_gemm_tile_shape(m, n, k)
+            rows.append({"N": n, "K": k, "M": m, "path": fp8bq.PATH_NAMES[path],
                          "us": round(us, 2), "GBps": round(gemm_bytes(m, n, k) / (us * 1e-6) / 1e9, 1),
                          "TFLOPs": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)})
             print(f"bench: sweep N={n} K={k} M={m}: {us:.2f} us", file=sys.stderr, flush=True)

@@ -130,6 +130,16 @@ enum {
 int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K);
 
 /*
+ * The tile shape the LDS-tiled kernel takes for (M, N, K), as the
+ * FP8BQ_PATH_TILED_* value fp8bq_gemm_forced accepts (fp8bq_gemm uses it
+ * for M > 64; any M >= 1 is answered): the shape with the least grid
+ * rounds on the 256 CUs times measured step cost. FP8BQ_PATH_NONE for
+ * M == 0 or N == 0, a negative status for invalid sizes. Host-only: no
+ * device is needed.
+ */
+int fp8bq_gemm_tile_shape(int64_t M, int64_t N, int64_t K);
+
+/*
  * fp8bq_gemm with the kernel path forced (FP8BQ_PATH_STREAM requires
  * M <= 128, as two launches past 64 tokens; FP8BQ_PATH_TILED and the
  * FP8BQ_PATH_TILED_* shapes accept any M). For cross-checking the paths and

@@ -28,7 +28,11 @@ PATH_NONE, PATH_STREAM, PATH_TILED = 0, 1, 2
 # tile shapes of the tiled kernel (tokens x weight rows), for gemm_forced
 PATH_TILED_128x128, PATH_TILED_128x256, PATH_TILED_192x256, PATH_TILED_256x256 = 3, 4, 5, 6
 PATH_TILED_64x128, PATH_TILED_128x64, PATH_TILED_64x64 = 7, 8, 9
-PATH_NAMES = {PATH_NONE: "none", PATH_STREAM: "stream", PATH_TILED: "tiled"}
+PATH_NAMES = {PATH_NONE: "none", PATH_STREAM: "stream", PATH_TILED: "tiled",
+              PATH_TILED_128x128: "tiled 128x128", PATH_TILED_128x256: "tiled 128x256",
+              PATH_TILED_192x256: "tiled 192x256", PATH_TILED_256x256: "tiled 256x256",
+              PATH_TILED_64x128: "tiled 64x128", PATH_TILED_128x64: "tiled 128x64", PATH_TILED_64x64: "tiled 64x64"}
+
 
 # Every symbol the C ABI exports (kept in step with include/fp8bq.h).
 EXPORTS = (
@@ -37,6 +41,7 @@ EXPORTS = (
     "fp8bq_gemm",
     "fp8bq_gemm_path",
     "fp8bq_gemm_forced",
+    "fp8bq_gemm_tile_shape",
     "fp8bq_gemm_fused",
     "fp8bq_gemm_w8a16",
     "fp8bq_topk_workspace_bytes",
@@ -73,6 +78,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_gemm.argtypes = [i64, i64, i64, vp, fp, vp, fp, vp, vp]
         L.fp8bq_gemm_forced.argtypes = [ctypes.c_int, i64, i64, i64, vp, fp, vp, fp, vp, vp]
         L.fp8bq_gemm_path.argtypes = [i64, i64, i64]
+        L.fp8bq_gemm_tile_shape.argtypes = [i64, i64, i64]
         L.fp8bq_gemm_w8a16.argtypes = [i64, i64, i64, vp, vp, fp, vp, vp]
         L.fp8bq_gemm_fused.argtypes = [i64, i64, i64, vp, vp, fp, vp, vp]
         L.fp8bq_topk_workspace_bytes.argtypes = [i64, i64, i64]
@@ -86,6 +92,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_status_string.argtypes = [ctypes.c_int]
         L.fp8bq_status_string.restype = ctypes.c_char_p
         for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path",
+                     "fp8bq_gemm_tile_shape",
                      "fp8bq_gemm_w8a16", "fp8bq_gemm_fused", "fp8bq_topk_bf16", "fp8bq_rescore_bf16",
                      "fp8bq_mb_read", "fp8bq_mb_empty", "fp8bq_mb_mfma_e4m3"):
             getattr(L, name).restype = ctypes.c_int

@@ -140,6 +140,13 @@ int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K) {
   return gemm_path(M);
 }
 
+int fp8bq_gemm_tile_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
+  if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BQ_PATH_NONE;
+  return FP8BQ_PATH_TILED_128x128 + fp8bq::tiled_shape(M, N);
+}
+
 int fp8bq_gemm_fused(int64_t M, int64_t N, int64_t K, const void* A_bf16, const void* W_fp8, const float* W_scales,
                      void* C_bf16, void* stream) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;

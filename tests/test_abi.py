@@ -30,7 +30,8 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert _declared() == {"fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_path",
-                           "fp8bq_gemm_forced", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16", "fp8bq_topk_workspace_bytes",
+                           "fp8bq_gemm_forced", "fp8bq_gemm_tile_shape", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16",
+                           "fp8bq_topk_workspace_bytes",
                            "fp8bq_topk_bf16", "fp8bq_rescore_bf16", "fp8bq_mb_read", "fp8bq_mb_empty",
                            "fp8bq_mb_mfma_e4m3", "fp8bq_status_string"}
 
@@ -250,3 +251,33 @@ def test_measurement_kernel_argument_errors(fp8bq):
     assert L.fp8bq_mb_mfma_e4m3(1, 1, 256, p, None) == -2
     assert L.fp8bq_mb_mfma_e4m3(1, 1, 0x38, None, None) == -1
     assert L.fp8bq_mb_mfma_e4m3(1, 1, 0x38, p + 2, None) == -3
+
+
+def test_tile_shape_rule_takes_the_measured_choices(fp8bq):
+    """The tiled kernel's shape rule (least grid rounds x measured step
+    cost) on the points where the shapes were timed side by side: each
+    expectation is the shape that measured fastest there."""
+    L = fp8bq.lib()
+    shape = lambda m, n, k: fp8bq.PATH_NAMES[L.fp8bq_gemm_tile_shape(m, n, k)]
+    assert shape(3465, 17408, 5120) == "tiled 256x256"  # 952 tiles, 4 rounds
+    assert shape(3465, 5120, 8704) == "tiled 192x256"  # 380 tiles, 2 rounds (256 x 256: 280, 1.09)
+    assert shape(2048, 5120, 3072) == "tiled 192x256"
+    assert shape(4096, 7168, 5120) == "tiled 256x256"
+    assert shape(1024, 8192, 5120) == "tiled 128x256"
+    assert shape(1024, 17408, 5120) == "tiled 192x256"
+    for m in (65, 96, 128):
+        assert shape(m, 17408, 5120) == "tiled 128x128", m  # 136 tiles; smaller ones overflow a round
+        for n, k in ((5120, 3072), (5120, 8704), (7168, 5120), (8192, 5120)):
+            assert shape(m, n, k) == "tiled 64x64", (m, n)  # 160..256 tiles, one round
+    assert shape(192, 17408, 5120) == "tiled 64x128"
+    assert shape(192, 5120, 8704) == "tiled 64x64"
+    assert shape(192, 7168, 5120) == "tiled 128x64"
+    assert shape(192, 8192, 5120) == "tiled 128x64"
+    assert shape(256, 5120, 8704) == "tiled 64x128"  # equal cost to 128 x 64, equal tiles: first in order
+    # every answer is a shape fp8bq_gemm_forced accepts; sizes as for the GEMM
+    for m in (1, 64, 65, 300, 3465, 100000):
+        for n in (1, 127, 5120, 17408, 152064):
+            assert fp8bq.PATH_TILED_128x128 <= L.fp8bq_gemm_tile_shape(m, n, 5120) <= fp8bq.PATH_TILED_64x64
+    assert L.fp8bq_gemm_tile_shape(0, 5120, 5120) == fp8bq.PATH_NONE
+    assert L.fp8bq_gemm_tile_shape(1, 5120, 100) == -2
+    assert L.fp8bq_gemm_tile_shape(-1, 5120, 128) == -2
