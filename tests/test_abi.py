@@ -255,8 +255,9 @@ def test_measurement_kernel_argument_errors(fp8bq):
 
 def test_tile_shape_rule_takes_the_measured_choices(fp8bq):
     """The tiled kernel's shape rule (least grid rounds x measured step
-    cost) on the points where the shapes were timed side by side: each
-    expectation is the shape that measured fastest there."""
+    cost) on the 25 points where the shapes were timed side by side (each
+    expectation is the shape that measured fastest there), then its
+    tie-break and its range."""
     L = fp8bq.lib()
     shape = lambda m, n, k: fp8bq.PATH_NAMES[L.fp8bq_gemm_tile_shape(m, n, k)]
     assert shape(3465, 17408, 5120) == "tiled 256x256"  # 952 tiles, 4 rounds
