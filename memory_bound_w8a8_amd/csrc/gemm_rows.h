@@ -62,21 +62,8 @@ enum ActForm : int {
 // an all-zero group), code = RNE(clamp(x / s, +-448)). Returns the 32 codes
 // in operand byte order and sets the scale.
 //
-// The quotient uses the correctly rounded reciprocal y = 1 / s once per
-// group and, per value, q0 = x y, r = fma(-q0, s, x) (exact), q = q0 if
-// r == 0 else fma(r, y, q0). An exhaustive GPU check over every bf16 x and
-// every bf16 amax >= |x| found the e4m3 codes of this quotient equal to
-// those of the IEEE division whenever amax >= 2^-104; below 2^-96 the IEEE
-// division is used instead. fma(r, y, q0) equals q0 when r == 0 and x != 0
-// (adding a zero to a non-zero value is exact) and has the sign of x
-// otherwise, so the select is written as copysign(fma(r, y, q0), x), which
-// differs only for x = -0, where it keeps the sign as the select did.
-__device__ __forceinline__ float quotient_e4m3_range(float x, float s, float y) {
-  const float q0 = x * y;
-  const float r = fmaf(-q0, s, x);
-  return fminf(fmaxf(copysignf(fmaf(r, y, q0), x), -kE4m3Max), kE4m3Max);
-}
-
+// The quotient is quotient_e4m3_range (device_common.h): equal in code to
+// the IEEE division x / s whenever amax >= 2^-96; below, the division.
 __device__ __forceinline__ v8i quant_group_operand(const v4u (&raw)[4], float* scale) {
   float x[32];
 #pragma unroll

@@ -80,6 +80,46 @@ def test_quant_act_random_bf16_bit_patterns():
     _assert_bitexact(_act_gpu(a), quant_act_ref(a), "random bit patterns")
 
 
+def _band_groups():
+    """Groups whose first entry is a chosen maximum a and whose other
+    entries run over every bf16 value x with a * 2^-19 <= |x| <= a, both
+    signs (everything that quantises to a non-zero code, and the first
+    values that round to zero), for about a thousand maxima: every exponent
+    field 0..254 with mantissa fields 0x00, 0x01, 0x40, 0x7f (subnormal
+    maxima included, zero excluded). Returns bf16 [rows, 8192]."""
+    pos = np.arange(1, 0x7F80, dtype=np.uint32)  # positive finite bf16 patterns
+    vals = (pos << 16).view(np.float32)
+    groups = []
+    for e in range(0, 255):
+        for mant in (0x00, 0x01, 0x40, 0x7F):
+            p = (e << 7) | mant
+            if p == 0:
+                continue
+            a = np.float32(((np.uint32(p) << 16)).view(np.float32))
+            sel = pos[(vals <= a) & (vals >= a * np.float32(2.0 ** -19))]
+            xs = np.concatenate([sel, sel | 0x8000]).astype(np.uint16)
+            n_g = -(-xs.size // 127)
+            body = np.zeros(n_g * 127, dtype=np.uint16)
+            body[: xs.size] = xs
+            g = np.empty((n_g, 128), dtype=np.uint16)
+            g[:, 0] = p
+            g[:, 1:] = body.reshape(n_g, 127)
+            groups.append(g)
+    g = np.concatenate(groups)
+    rows = -(-g.shape[0] // 64)
+    out = np.zeros((rows * 64, 128), dtype=np.uint16)
+    out[: g.shape[0]] = g
+    return torch.from_numpy(out.reshape(rows, 64 * 128).view(np.int16)).view(torch.bfloat16)
+
+
+def test_quant_act_every_bf16_value_under_a_thousand_maxima():
+    # the kernel forms x / s from the reciprocal of s and one fma correction
+    # (IEEE division only below amax = 2^-96); its codes must still be those
+    # of the correctly rounded division for every input it can see
+    a = _band_groups()
+    _assert_bitexact(_act_gpu(a), quant_act_ref(a), "bf16 values under chosen maxima")
+
+
 def test_quant_act_empty_is_noop():
     a_q, a_s = fp8bq.quant_act(torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda"))
     assert a_q.shape == (0, 256) and a_s.shape == (0, 2)
