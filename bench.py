@@ -268,11 +268,19 @@ def two_stage(reps=50):
         val = torch.empty((m, kk), dtype=torch.bfloat16, device=dev)
         scores = torch.empty((m, kk), dtype=torch.float32, device=dev)
         pick = torch.empty((m,), dtype=torch.int32, device=dev)
+        hq = torch.empty((m, k), dtype=torch.uint8, device=dev)
+        hs = torch.empty((m, k // 128), dtype=torch.float32, device=dev)
 
         def coarse():
-            st = L.fp8bq_gemm_fused(m, v, k, h.data_ptr(), wq.data_ptr(), ws.data_ptr(), logits.data_ptr(), s)
+            # the same logits either way (bitwise); the fused launch up to 8
+            # tokens, quantisation + GEMM beyond, as fp8bq.two_stage does
+            if m <= fp8bq.TWO_STAGE_FUSED_MAX_M:
+                st = L.fp8bq_gemm_fused(m, v, k, h.data_ptr(), wq.data_ptr(), ws.data_ptr(), logits.data_ptr(), s)
+            else:
+                st = L.fp8bq_quant_act(m, k, h.data_ptr(), hq.data_ptr(), hs.data_ptr(), s) or L.fp8bq_gemm(
+                    m, v, k, hq.data_ptr(), hs.data_ptr(), wq.data_ptr(), ws.data_ptr(), logits.data_ptr(), s)
             if st:
-                raise fp8bq.Fp8bqError("fp8bq_gemm_fused", st)
+                raise fp8bq.Fp8bqError("coarse logits", st)
 
         def select():
             st = L.fp8bq_topk_bf16(m, v, kk, logits.data_ptr(), work.data_ptr(), wsb, idx.data_ptr(),

@@ -295,12 +295,24 @@ def rescore(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor):
     return scores, pick
 
 
+# Largest token count whose coarse logits two_stage() takes from the fused
+# launch; beyond it, quantisation + GEMM (bitwise the same logits) measured
+# faster at the vocabulary size (V = 152064, K = 5120: 127 vs 131 us at
+# M = 9, 135 vs 144 at M = 16; the fused launch wins or ties up to 8).
+TWO_STAGE_FUSED_MAX_M = 8
+
+
 def two_stage(h: torch.Tensor, w_q, w_s, w_bf16: torch.Tensor, k: int, workspace: torch.Tensor = None):
-    """Two-stage vocabulary scoring of hidden states h bf16 [M, K] (M <= 16):
-    coarse logits by the fused block-FP8 GEMM against (w_q, w_s), their exact
-    top-k, exact scores of those k against the bf16 projection w_bf16 [V, K].
-    Returns (pick int32 [M], idx int32 [M, k], scores fp32 [M, k])."""
-    logits = gemm_fused(h, w_q, w_s)
+    """Two-stage vocabulary scoring of hidden states h bf16 [M, K]: coarse
+    logits by the block-FP8 GEMM of the quantised h against (w_q, w_s),
+    their exact top-k, exact scores of those k against the bf16 projection
+    w_bf16 [V, K]. Returns (pick int32 [M], idx int32 [M, k], scores fp32
+    [M, k])."""
+    _need(h, "h", torch.bfloat16, 2)
+    if h.shape[0] <= TWO_STAGE_FUSED_MAX_M:
+        logits = gemm_fused(h, w_q, w_s)
+    else:
+        logits = gemm(*quant_act(h), w_q, w_s)
     idx, _ = topk(logits, k, workspace)
     scores, pick = rescore(h, w_bf16, idx)
     return pick, idx, scores

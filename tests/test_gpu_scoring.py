@@ -180,7 +180,8 @@ def _gemm_tol(ref: np.ndarray) -> np.ndarray:
     return RMS_TOL * rms + BF16_U * np.abs(ref)
 
 
-@pytest.mark.parametrize("m,v,kdim,k", [(1, 20000, 1024, 64), (5, 9000 + 77, 2048, 50), (16, 4096, 512, 8)])
+@pytest.mark.parametrize("m,v,kdim,k", [(1, 20000, 1024, 64), (5, 9000 + 77, 2048, 50), (16, 4096, 512, 8),
+                                        (24, 3000, 1024, 16)])
 def test_two_stage_pipeline(m, v, kdim, k):
     # oracle: coarse logits = block-FP8 GEMM of the quantised hidden state and
     # the FP8 projection; exact scores = bf16 hidden state x bf16 projection
