@@ -193,6 +193,10 @@ def _full_cases():
     cases = []
     for n, k in workloads.SHAPES:  # grouped by shape: one weight upload each
         ms = [1, 8, 64]
+        if (n, k) == (5120, 3072):
+            ms = [1, 8, 64, 256]  # 64 x 128 tiles
+        if (n, k) == (8192, 5120):
+            ms = [1, 8, 64, 192]  # 128 x 64 tiles
         if (n, k) == (17408, 5120):
             ms = list(range(1, 9)) + [16, 32, 64]
         if (n, k) == (5120, 8704):
