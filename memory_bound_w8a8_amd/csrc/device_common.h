@@ -90,16 +90,20 @@ __device__ __forceinline__ float scaled_clamped(float x, float s) {
   return fminf(fmaxf(x / s, -kE4m3Max), kE4m3Max);
 }
 
-// Exact-in-code quotient for e4m3 quantisation. The quotient uses the correctly rounded reciprocal y = 1 / s once per
-// group and, per value, q0 = x y, r = fma(-q0, s, x) (exact), q = q0 if
-// r == 0 else fma(r, y, q0). An exhaustive GPU check over every bf16 x and
-// every bf16 amax >= |x| found the e4m3 codes of this quotient equal to
-// those of the IEEE division whenever amax >= 2^-104 (the GPU tests repeat
-// it for every bf16 x within 19 binades below a thousand maxima across the
-// exponent range); callers take the IEEE division below amax = 2^-96. fma(r, y, q0) equals q0 when r == 0 and x != 0
-// (adding a zero to a non-zero value is exact) and has the sign of x
-// otherwise, so the select is written as copysign(fma(r, y, q0), x), which
-// differs only for x = -0, where it keeps the sign as the select did.
+// Exact-in-code quotient for e4m3 quantisation: Markstein's fma-based
+// correction of a reciprocal-based quotient. The correctly rounded
+// reciprocal y = 1 / s is formed once per group and, per value, q0 = x y,
+// r = fma(-q0, s, x) (the exact residual), q = fma(r, y, q0). q is not
+// always the correctly rounded x / s, but its e4m3 code (after the clamp) is
+// that of the IEEE division for every bf16 x with |x| <= amax and every
+// bf16 amax >= 2^-96: tests/quotient_check.c checks all 5.2e8 such pairs on
+// the host, and the GPU tests compare the kernels' codes with the oracle for
+// every bf16 x within 19 binades below every bf16 amax mantissa at 29
+// exponents (subnormal maxima and the 2^-104 .. 2^-96 neighbourhood
+// included). Callers take the IEEE division below amax = 2^-96.
+// fma(r, y, q0) equals q0 when r == 0 and x != 0 (adding a zero to a
+// non-zero value is exact) and has the sign of x otherwise; copysign(., x)
+// only fixes x = -0, whose quotient must stay -0.
 __device__ __forceinline__ float quotient_e4m3_range(float x, float s, float y) {
   const float q0 = x * y;
   const float r = fmaf(-q0, s, x);

@@ -192,17 +192,20 @@ def test_k_zero_writes_zeros_and_m_zero_is_noop():
 def _full_cases():
     cases = []
     for n, k in workloads.SHAPES:  # grouped by shape: one weight upload each
-        ms = [1, 8, 64]
+        # every shape: decode, verify, the concurrent batches 16 / 32 / 64
+        ms = [1, 8, 16, 32, 64]
         if (n, k) == (5120, 3072):
-            ms = [1, 8, 64, 256]  # 64 x 128 tiles
+            # both token classes of the 2-tile, 3-groups-per-wave instances
+            # (9..16 and 17..32), and 64 x 128 tiles at 256
+            ms = [1, 8, 9, 12, 16, 17, 24, 32, 64, 256]
         if (n, k) == (8192, 5120):
-            ms = [1, 8, 64, 192]  # 128 x 64 tiles
+            ms = [1, 8, 16, 32, 64, 192]  # 128 x 64 tiles
         if (n, k) == (17408, 5120):
             ms = list(range(1, 9)) + [16, 32, 64]
         if (n, k) == (5120, 8704):
-            ms = [1, 8, 17, 32, 64, 65, 128]
+            ms = [1, 8, 16, 17, 32, 64, 65, 128]
         if (n, k) == (7168, 5120):
-            ms = [1, 8, 64, 100]
+            ms = [1, 8, 16, 32, 64, 100]
         if (n, k) in workloads.PREFILL_SHAPES:
             ms.append(workloads.PREFILL_M)
         cases += [(m, n, k) for m in ms]

@@ -77,3 +77,47 @@ def test_rescore_ref_exact_and_pick():
         best = max(range(kk), key=lambda j: (exact[j], -idx[i, j]))
         assert pick[i] == idx[i, best]
     assert pick[0] == 3  # the tie between rows 3 and 5 goes to row 3
+
+
+def _pattern_rank(b):
+    """The stated order read off a bf16 bit pattern directly: every pattern
+    with the sign bit clear ranks above every pattern with it set; among the
+    former a larger 15-bit magnitude field ranks higher, among the latter
+    lower. NaN and infinity patterns take their place by the same rule."""
+    b = int(b)
+    mag = b & 0x7FFF
+    return (1, mag) if b < 0x8000 else (0, -mag)
+
+
+def _brute_topk_any_pattern(bits_row, k):
+    items = sorted(range(len(bits_row)), key=lambda i: (_pattern_rank(bits_row[i]), -i), reverse=True)
+    return items[:k]
+
+
+def test_pattern_rank_is_the_value_order_on_non_nan_patterns():
+    # the tuple rank above is the numeric order (infinities at the ends, +0
+    # over -0) wherever a value exists: checked against torch's decoding
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    nan = ((b & 0x7F80) == 0x7F80) & ((b & 0x7F) != 0)
+    b = b[~nan]
+    vals = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float().numpy()
+    order = sorted(range(b.size), key=lambda i: _pattern_rank(b[i]))
+    v = vals[order]
+    assert np.all(v[1:] >= v[:-1])
+    assert np.isneginf(v[0]) and np.isposinf(v[-1])
+
+
+@pytest.mark.parametrize("v,k,seed", [(64, 10, 11), (300, 64, 12), (1000, 256, 13), (97, 97, 14)])
+def test_topk_ref_on_inf_and_nan_patterns(v, k, seed):
+    rng = np.random.default_rng(seed)
+    special = np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC0, 0x7F81, 0xFFFF, 0x7FFF, 0x0000, 0x8000, 0x3F80, 0xBF80],
+                       dtype=np.uint16)
+    bits = np.stack([
+        rng.integers(0, 1 << 16, size=v).astype(np.uint16),  # every pattern class, NaN and Inf included
+        rng.choice(special, size=v),  # mostly infinities, NaNs and zeros: many ties
+        np.where(rng.random(v) < 0.5, rng.choice(special, size=v), rng.integers(0, 1 << 16, size=v)).astype(np.uint16),
+    ])
+    idx, vals = topk_ref(bits, k)
+    for i in range(bits.shape[0]):
+        assert list(idx[i]) == _brute_topk_any_pattern(bits[i], k)
+        assert np.array_equal(vals[i], bits[i][idx[i]])
