@@ -24,7 +24,8 @@
  *   - All tensor pointers are DEVICE pointers on the current HIP device; all
  *     tensors are dense row-major. The caller owns every buffer; the library
  *     allocates nothing, keeps no pointer after return and has no state
- *     beyond a per-device capability check.
+ *     beyond a per-device capability check and the static scratch array of
+ *     fp8bq_topk_bf16_noalloc (with its per-device address).
  *   - `stream` is a hipStream_t (NULL = the null stream). Calls enqueue work
  *     on it and return without synchronising; faults during execution
  *     surface at the caller's next synchronisation.
@@ -50,7 +51,9 @@ typedef enum fp8bq_status {
     FP8BQ_ERR_SHAPE = -2,  /* a size is negative, K % 128 != 0, or too large  */
     FP8BQ_ERR_ALIGN = -3,  /* code/bf16 pointer not 16-B aligned, fp32 not 4-B */
     FP8BQ_ERR_DEVICE = -4, /* no HIP device, or the current device is not gfx950 */
-    FP8BQ_ERR_LAUNCH = -5  /* the HIP runtime rejected a kernel launch        */
+    FP8BQ_ERR_LAUNCH = -5, /* the HIP runtime rejected a kernel launch        */
+    FP8BQ_ERR_SCRATCH = -6 /* the request needs more than the library's static
+                              scratch buffer (fp8bq_topk_bf16_noalloc)       */
 } fp8bq_status;
 
 /*
@@ -235,6 +238,28 @@ int64_t fp8bq_topk_workspace_bytes(int64_t M, int64_t V, int64_t k);
  */
 int fp8bq_topk_bf16(int64_t M, int64_t V, int64_t k, const void *logits_bf16, void *workspace,
                     int64_t workspace_bytes, int32_t *idx_out, void *val_bf16_out, void *stream);
+
+/*
+ * fp8bq_topk_bf16 for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops that must not call hipMalloc, harnesses
+ * that forbid allocation. It takes no workspace; its kernels use a static
+ * device array of the library instead, FP8BQ_TOPK_SCRATCH_BYTES (4 MiB) on
+ * each GPU it runs on, held until the process ends. Its address is looked
+ * up once per device on the first call there; the call allocates nothing.
+ *
+ *   logits_bf16, idx_out, val_bf16_out, k, M, V: as fp8bq_topk_bf16, with
+ *   identical results (bitwise).
+ * Every call on one GPU shares that GPU's array: calls that may overlap on
+ * one GPU (different streams, or host threads without ordering) race and
+ * must be ordered by the caller. The array's contents need no clearing (the
+ * kernels ignore them on entry) and are unspecified after a call.
+ * Errors: as fp8bq_topk_bf16 (no workspace arguments), plus
+ * FP8BQ_ERR_SCRATCH when fp8bq_topk_workspace_bytes(M, V, k) exceeds
+ * FP8BQ_TOPK_SCRATCH_BYTES (e.g. V = 152064, k = 64 serves M <= 199).
+ */
+#define FP8BQ_TOPK_SCRATCH_BYTES (4 << 20)
+int fp8bq_topk_bf16_noalloc(int64_t M, int64_t V, int64_t k, const void *logits_bf16, int32_t *idx_out,
+                            void *val_bf16_out, void *stream);
 
 /*
  * Exact scores of the survivors and each row's pick.

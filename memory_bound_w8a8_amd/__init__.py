@@ -46,6 +46,7 @@ EXPORTS = (
     "fp8bq_gemm_w8a16",
     "fp8bq_topk_workspace_bytes",
     "fp8bq_topk_bf16",
+    "fp8bq_topk_bf16_noalloc",
     "fp8bq_rescore_bf16",
     "fp8bq_mb_read",
     "fp8bq_mb_empty",
@@ -84,6 +85,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_topk_workspace_bytes.argtypes = [i64, i64, i64]
         L.fp8bq_topk_workspace_bytes.restype = i64
         L.fp8bq_topk_bf16.argtypes = [i64, i64, i64, vp, vp, i64, vp, vp, vp]
+        L.fp8bq_topk_bf16_noalloc.argtypes = [i64, i64, i64, vp, vp, vp, vp]
         L.fp8bq_rescore_bf16.argtypes = [i64, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         ci = ctypes.c_int
         L.fp8bq_mb_read.argtypes = [vp, i64, ci, vp, vp]
@@ -93,7 +95,8 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_status_string.restype = ctypes.c_char_p
         for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path",
                      "fp8bq_gemm_tile_shape",
-                     "fp8bq_gemm_w8a16", "fp8bq_gemm_fused", "fp8bq_topk_bf16", "fp8bq_rescore_bf16",
+                     "fp8bq_gemm_w8a16", "fp8bq_gemm_fused", "fp8bq_topk_bf16", "fp8bq_topk_bf16_noalloc",
+                     "fp8bq_rescore_bf16",
                      "fp8bq_mb_read", "fp8bq_mb_empty", "fp8bq_mb_mfma_e4m3"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -269,6 +272,27 @@ def topk(logits: torch.Tensor, k: int, workspace: torch.Tensor = None):
         st = lib().fp8bq_topk_bf16(m, v, int(k), _ptr(logits), _ptr(workspace), workspace.numel(), _ptr(idx),
                                    _ptr(val), _stream(logits))
     _check("fp8bq_topk_bf16", st)
+    return idx, val
+
+
+# Bytes of the library's static scratch array used by topk_noalloc.
+TOPK_SCRATCH_BYTES = 4 << 20
+
+
+def topk_noalloc(logits: torch.Tensor, k: int, idx: torch.Tensor, val: torch.Tensor):
+    """topk() into caller-provided outputs (int32 idx [M, k], bf16 val [M, k])
+    through the entry point that allocates nothing: its workspace is the
+    library's static per-GPU scratch array (calls on one GPU must not
+    overlap). Returns (idx, val)."""
+    _need(logits, "logits", torch.bfloat16, 2)
+    _need(idx, "idx", torch.int32, 2)
+    _need(val, "val", torch.bfloat16, 2)
+    m, v = logits.shape
+    if tuple(idx.shape) != (m, k) or tuple(val.shape) != (m, k):
+        raise ValueError(f"idx and val must be [{m}, {k}]")
+    with torch.cuda.device(logits.device):
+        st = lib().fp8bq_topk_bf16_noalloc(m, v, int(k), _ptr(logits), _ptr(idx), _ptr(val), _stream(logits))
+    _check("fp8bq_topk_bf16_noalloc", st)
     return idx, val
 
 

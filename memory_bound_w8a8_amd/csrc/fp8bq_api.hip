@@ -208,6 +208,20 @@ int fp8bq_topk_bf16(int64_t M, int64_t V, int64_t k, const void* logits_bf16, vo
                                           static_cast<hipStream_t>(stream)));
 }
 
+int fp8bq_topk_bf16_noalloc(int64_t M, int64_t V, int64_t k, const void* logits_bf16, int32_t* idx_out,
+                            void* val_bf16_out, void* stream) {
+  if (M < 0 || V < 0 || V > kMaxIndex || k < 1 || k > kTopkMaxK || k > V || !product_ok(M, V)) return FP8BQ_ERR_SHAPE;
+  if (fp8bq::topk_grid_blocks(M, V, k) > kMaxGridBlocks) return FP8BQ_ERR_SHAPE;
+  if (M == 0) return FP8BQ_OK;
+  if (fp8bq::topk_workspace_bytes(M, V, k) > fp8bq::kTopkScratchBytes) return FP8BQ_ERR_SCRATCH;
+  if (logits_bf16 == nullptr || idx_out == nullptr || val_bf16_out == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(logits_bf16, 16) || !aligned(idx_out, 4) || !aligned(val_bf16_out, 16)) return FP8BQ_ERR_ALIGN;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(fp8bq::launch_topk_noalloc(M, V, static_cast<int>(k), logits_bf16, idx_out, val_bf16_out,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void* h_bf16, const void* W_bf16,
                        const int32_t* idx, float* scores_out, int32_t* pick_out, void* stream) {
   if (M < 0 || K < 0 || K % 8 != 0 || V < 0 || V > kMaxIndex || k < 1) return FP8BQ_ERR_SHAPE;
@@ -232,6 +246,7 @@ const char* fp8bq_status_string(int status) {
     case FP8BQ_ERR_ALIGN: return "misaligned pointer (codes/bf16 need 16 B, fp32 scales 4 B)";
     case FP8BQ_ERR_DEVICE: return "no usable HIP device (gfx950 required)";
     case FP8BQ_ERR_LAUNCH: return "kernel launch failed";
+    case FP8BQ_ERR_SCRATCH: return "request needs more than the library's static scratch buffer (4 MiB per GPU)";
     default: return "unknown status";
   }
 }

@@ -40,6 +40,13 @@ int64_t topk_grid_blocks(int64_t m, int64_t v, int64_t k);
 int64_t rescore_grid_blocks(int64_t m, int64_t k);
 hipError_t launch_topk(int64_t m, int64_t v, int k, const void* logits, void* workspace, int* idx, void* val,
                        hipStream_t stream);
+// fp8bq_topk_bf16_noalloc: the same kernels with the library's static
+// per-GPU scratch array (kTopkScratchBytes) as their workspace. The caller
+// checks topk_workspace_bytes(m, v, k) <= kTopkScratchBytes first.
+constexpr int64_t kTopkScratchBytes = int64_t(4) << 20;
+hipError_t topk_scratch_address(void** out);
+hipError_t launch_topk_noalloc(int64_t m, int64_t v, int k, const void* logits, int* idx, void* val,
+                               hipStream_t stream);
 hipError_t launch_rescore(int64_t m, int64_t kdim, int64_t v, int64_t k, const void* h, const void* w,
                           const int* idx, float* scores, int* pick, hipStream_t stream);
 

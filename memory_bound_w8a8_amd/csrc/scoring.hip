@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -398,6 +400,49 @@ hipError_t launch_topk(int64_t m, int64_t v, int k, const void* logits, void* wo
     b = t;
   }
   return e;
+}
+
+// Workspace of fp8bq_topk_bf16_noalloc: a static device array, one copy per
+// GPU for the life of the process. In host code `scratch` names a host-side
+// stand-in, not the device memory: the device address comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// and kept per device; only that pointer is ever passed to a kernel. The top-k
+// kernels ignore the workspace's contents on entry, so nothing is cleared.
+// Every no-allocation call on one GPU shares the array: calls that overlap
+// on one GPU (different streams, or threads without ordering) race.
+static __device__ __align__(256) unsigned char scratch[kTopkScratchBytes];
+
+namespace {
+
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchMaxDevices];
+
+}  // namespace
+
+hipError_t topk_scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_topk_noalloc(int64_t m, int64_t v, int k, const void* logits, int* idx, void* val,
+                               hipStream_t stream) {
+  if (topk_workspace_bytes(m, v, k) > kTopkScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = topk_scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_topk(m, v, k, logits, ws, idx, val, stream);
 }
 
 int64_t rescore_grid_blocks(int64_t m, int64_t k) { return m * ((k + kRescoreWaves - 1) / kRescoreWaves); }

@@ -32,7 +32,7 @@ def test_header_declares_the_abi():
     assert _declared() == {"fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_path",
                            "fp8bq_gemm_forced", "fp8bq_gemm_tile_shape", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16",
                            "fp8bq_topk_workspace_bytes",
-                           "fp8bq_topk_bf16", "fp8bq_rescore_bf16", "fp8bq_mb_read", "fp8bq_mb_empty",
+                           "fp8bq_topk_bf16", "fp8bq_topk_bf16_noalloc", "fp8bq_rescore_bf16", "fp8bq_mb_read", "fp8bq_mb_empty",
                            "fp8bq_mb_mfma_e4m3", "fp8bq_status_string"}
 
 
@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(fp8bq):
 
 def test_status_strings(fp8bq):
     L = fp8bq.lib()
-    for st in (0, -1, -2, -3, -4, -5):
+    for st in (0, -1, -2, -3, -4, -5, -6):
         s = L.fp8bq_status_string(st).decode()
         assert s and s != "unknown status"
     assert L.fp8bq_status_string(42).decode() == "unknown status"
@@ -150,6 +150,29 @@ def test_topk_workspace_size(fp8bq):
     assert L.fp8bq_topk_workspace_bytes(1, 100, 101) == -2
     assert L.fp8bq_topk_workspace_bytes(-1, 100, 5) == -2
     assert L.fp8bq_topk_workspace_bytes(1, 1 << 31, 5) == -2
+
+
+def test_topk_noalloc_errors(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    f = L.fp8bq_topk_bf16_noalloc
+    scratch = fp8bq.TOPK_SCRATCH_BYTES
+    assert scratch == 4 << 20
+    # largest M whose workspace fits the 4 MiB scratch at V = 152064, k = 64
+    per_row = L.fp8bq_topk_workspace_bytes(1, 152064, 64)
+    assert per_row * 199 <= scratch < per_row * 200
+    assert f(200, 152064, 64, p, p, p, None) == -6  # too large for the scratch array
+    assert f(2, 1000, 0, p, p, p, None) == -2
+    assert f(2, 1000, 257, p, p, p, None) == -2
+    assert f(2, 7, 8, p, p, p, None) == -2
+    assert f(-1, 1000, 8, p, p, p, None) == -2
+    assert f(0, 1000, 8, None, None, None, None) == 0
+    assert f(2, 1000, 8, None, p, p, None) == -1
+    assert f(2, 1000, 8, p, None, p, None) == -1
+    assert f(2, 1000, 8, p, p, None, None) == -1
+    assert f(2, 1000, 8, p + 2, p, p, None) == -3
+    assert f(2, 1000, 8, p, p + 2, p, None) == -3
+    assert f(2, 1000, 8, p, p, p + 2, None) == -3
 
 
 def test_topk_errors(fp8bq):
