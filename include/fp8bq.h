@@ -284,7 +284,6 @@ int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void *h
                        const void *W_bf16, const int32_t *idx, float *scores_out,
                        int32_t *pick_out, void *stream);
 
-/* Human-readable name of a status code; never NULL. */
 /*
  * Measurement kernels: what this machine delivers, to read the GEMM's
  * roofline fractions against besides the published peaks (page 1, SmartX
@@ -313,6 +312,7 @@ int fp8bq_mb_read(const void *buf, int64_t bytes, int grid, unsigned *sink, void
 int fp8bq_mb_empty(int grid, int block, void *stream);
 int fp8bq_mb_mfma_e4m3(int grid, int iters, int code, float *sink, void *stream);
 
+/* Human-readable name of a status code; never NULL. */
 const char *fp8bq_status_string(int status);
 
 #ifdef __cplusplus
