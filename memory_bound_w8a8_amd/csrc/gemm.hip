@@ -163,6 +163,26 @@ hipError_t tiled_instance(int64_t m, int64_t n, int64_t k, const void* aq, const
   return hipGetLastError();
 }
 
+// The 8-wave two-stage tiles (192 x 256, 256 x 256): gemm_tiled2_kernel,
+// unclamped when every row of every tile exists once the last token tile is
+// shifted back (M >= BM, N a multiple of BN, a tile's rows within 32-bit
+// copy offsets).
+template <int BM, int BN>
+hipError_t tiled2_instance(int64_t m, int64_t n, int64_t k, const void* aq, const float* as, const void* wq,
+                           const float* ws, void* c, hipStream_t stream) {
+  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const bool exact = m >= BM && n % BN == 0 && k < (int64_t(1) << 23);
+  if (exact)
+    hipLaunchKernelGGL((gemm_tiled2_kernel<BM, BN, 2, 4, false>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0,
+                       stream, m, n, k, static_cast<const unsigned char*>(aq), as, static_cast<const unsigned char*>(wq),
+                       ws, static_cast<unsigned short*>(c));
+  else
+    hipLaunchKernelGGL((gemm_tiled2_kernel<BM, BN, 2, 4, true>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0,
+                       stream, m, n, k, static_cast<const unsigned char*>(aq), as, static_cast<const unsigned char*>(wq),
+                       ws, static_cast<unsigned short*>(c));
+  return hipGetLastError();
+}
+
 namespace {
 
 struct TileShape {
@@ -180,8 +200,8 @@ struct TileShape {
 constexpr TileShape kTileShapes[] = {
     {128, 128, 1, 85, 85, "gemm_tiled_kernel BM=128 BN=128 4 waves 3 stages"},
     {128, 256, 1, 115, 115, "gemm_tiled_kernel BM=128 BN=256 8 waves 3 stages"},
-    {192, 256, 1, 150, 150, "gemm_tiled_kernel BM=192 BN=256 8 waves 2 stages"},
-    {256, 256, 1, 190, 190, "gemm_tiled_kernel BM=256 BN=256 8 waves 2 stages"},
+    {192, 256, 1, 150, 150, "gemm_tiled2_kernel BM=192 BN=256 8 waves 2 stages"},
+    {256, 256, 1, 190, 190, "gemm_tiled2_kernel BM=256 BN=256 8 waves 2 stages"},
     {64, 128, 2, 60, 100, "gemm_tiled_kernel BM=64 BN=128 4 waves 3 stages"},
     {128, 64, 2, 60, 100, "gemm_tiled_kernel BM=128 BN=64 4 waves 3 stages"},
     {64, 64, 3, 52, 90, "gemm_tiled_kernel BM=64 BN=64 4 waves 3 stages"},
@@ -243,9 +263,9 @@ hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, co
     case 1:
       return tiled_instance<128, 256, 2, 4, 3>(m, n, k, aq, as, wq, ws, c, stream);
     case 2:
-      return tiled_instance<192, 256, 2, 4, 2>(m, n, k, aq, as, wq, ws, c, stream);
+      return tiled2_instance<192, 256>(m, n, k, aq, as, wq, ws, c, stream);
     case 3:
-      return tiled_instance<256, 256, 2, 4, 2>(m, n, k, aq, as, wq, ws, c, stream);
+      return tiled2_instance<256, 256>(m, n, k, aq, as, wq, ws, c, stream);
     case 4:
       return tiled_instance<64, 128, 1, 4, 3>(m, n, k, aq, as, wq, ws, c, stream);
     case 5:

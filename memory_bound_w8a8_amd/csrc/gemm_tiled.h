@@ -366,4 +366,278 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   }
 }
 
+// Two-stage variant for the tiles whose two LDS stages take most of the
+// 160 KB (192 x 256 and 256 x 256 tokens x weight rows, 8 waves). Same
+// tiling, copies, swizzle and per-group summation order as
+// gemm_tiled_kernel (results are bitwise equal), with the K step arranged
+// around what its profile showed to be the cost: LDS latency in front of the
+// MFMAs.
+//  - The token fragment of sub-tile j + 1 is read while sub-tile j's MFMAs
+//    run (registers freed for it: one DMA lane offset instead of one per
+//    chunk, the chunk bases in scalar registers; weight scales fetched 64
+//    groups at a time with a vector load and picked per step with
+//    v_readlane, so no scalar load shares the LDS wait counter in the loop).
+//  - The last token sub-tile's MFMAs are deferred across the step barrier:
+//    after the barrier a wave issues the next step's copies and fragment
+//    reads, then those MFMAs (operands already in registers), which cover
+//    the latency of the new reads; each weight fragment is refilled right
+//    after the MFMA that last uses it.
+//  - CLAMP = false (every row of the tile exists: M >= BM, N a multiple of
+//    BN): the last token tile is shifted back to end at row M - 1 and stores
+//    only the rows the previous tile does not, so no row is clamped and one
+//    lane offset serves every copy. CLAMP = true keeps the per-chunk clamped
+//    offsets of gemm_tiled_kernel.
+template <int BM, int BN, int WM, int WN, bool CLAMP>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_rows, int64_t n, int64_t k,
+                                                                   const unsigned char* __restrict__ aq,
+                                                                   const float* __restrict__ as,
+                                                                   const unsigned char* __restrict__ wq,
+                                                                   const float* __restrict__ ws,
+                                                                   unsigned short* __restrict__ c) {
+  constexpr int WAVES = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN, J = TM / 16, I = TN / 16;
+  static_assert(TN <= 128 && 128 % TN == 0, "a wave's weight rows must sit in one 128-row scale block");
+  static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "8-row load chunks spread over the waves");
+  static_assert(BM % 64 == 0 && BM <= 64 * WAVES, "scales: one dword per token, 64 tokens per wave");
+  static_assert(J >= 2, "at least two token sub-tiles per wave");
+  constexpr int kStageBytes = (BM + BN) * 128 + BM * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char lds0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds1[kStageBytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lrow = lane & 15;
+  const int quarter = lane >> 4;
+  const int wave_m = wave % WM;
+  const int wave_n = wave / WM;
+  const int64_t groups = k >> 7;
+
+  const int64_t m_tiles = (m_rows + BM - 1) / BM;
+  const int64_t n_tiles = (n + BN - 1) / BN;
+  int64_t tm, tn;
+  band_tile(xcd_tile(blockIdx.x, m_tiles * n_tiles), m_tiles, n_tiles, 8, &tm, &tn);
+  const int64_t m_own = tm * BM;  // first token row this tile stores
+  int64_t m0 = m_own;
+  if (!CLAMP && m0 + BM > m_rows) m0 = m_rows - BM;  // last token tile shifted back: every row valid
+  const int64_t n0 = tn * BN;
+
+  constexpr int A_CHUNKS = BM / 8 / WAVES;
+  constexpr int W_CHUNKS = BN / 8 / WAVES;
+  const int cr = lane >> 3;
+  const unsigned char* a_base = aq + m0 * k;
+  const unsigned char* w_base = wq + n0 * k;
+  // DMA lane offsets. Without clamping every chunk q uses the same lane
+  // offset (row cr of its 8-row chunk, 16-byte piece (lane % 8) ^ cr); the
+  // chunk's first row goes into the scalar base.
+  unsigned a_off[CLAMP ? A_CHUNKS : 1];
+  unsigned w_off[CLAMP ? W_CHUNKS : 1];
+  if constexpr (CLAMP) {
+#pragma unroll
+    for (int q = 0; q < A_CHUNKS; ++q) {
+      const int r = 8 * (wave + WAVES * q) + cr;
+      const int64_t row = m0 + r < m_rows ? r : m_rows - 1 - m0;
+      a_off[q] = static_cast<unsigned>(row * k + 16 * ((lane & 7) ^ (r & 7)));
+    }
+#pragma unroll
+    for (int q = 0; q < W_CHUNKS; ++q) {
+      const int r = 8 * (wave + WAVES * q) + cr;
+      const int64_t row = n0 + r < n ? r : n - 1 - n0;
+      w_off[q] = static_cast<unsigned>(row * k + 16 * ((lane & 7) ^ (r & 7)));
+    }
+  } else {
+    a_off[0] = static_cast<unsigned>(cr * k + 16 * ((lane & 7) ^ cr));
+    w_off[0] = a_off[0];
+  }
+  const bool copies_scales = wave < BM / 64;
+  const float* sa_base = as + m0 * groups;
+  const int sa_t = 64 * (copies_scales ? wave : 0) + lane;
+  const int64_t sa_r = (!CLAMP || m0 + sa_t < m_rows) ? sa_t : m_rows - 1 - m0;
+  const unsigned sa_off = static_cast<unsigned>(sa_r * groups);
+  int64_t wblock = n0 + TN * wave_n;
+  if (CLAMP) wblock = wblock < n ? wblock : n - 1;
+  const float* sw_src = ws + (wblock >> 7) * groups;
+  // The wave's weight scales, 64 groups at a time: lane l holds group
+  // 64 c + l (a vector load; steps read theirs with v_readlane, so no
+  // scalar load shares the LDS wait counter inside the K loop).
+  auto sw_chunk = [&](int64_t g0) -> float {
+    const int64_t gl = g0 + lane < groups ? g0 + lane : groups - 1;
+    float v = sw_src[gl];
+    asm volatile("" : "+v"(v));  // a per-lane vector value, not a scalar load
+    return v;
+  };
+
+  // Without clamping: the first row of every 8-row chunk this wave copies,
+  // as uniform pointers computed once (the per-step address is then one
+  // scalar add).
+  const unsigned char* a_chunk[CLAMP ? 1 : A_CHUNKS];
+  const unsigned char* w_chunk[CLAMP ? 1 : W_CHUNKS];
+  if constexpr (!CLAMP) {
+#pragma unroll
+    for (int q = 0; q < A_CHUNKS; ++q)
+      a_chunk[q] = static_cast<const unsigned char*>(uniform(a_base + static_cast<int64_t>(8 * (wave + WAVES * q)) * k));
+#pragma unroll
+    for (int q = 0; q < W_CHUNKS; ++q)
+      w_chunk[q] = static_cast<const unsigned char*>(uniform(w_base + static_cast<int64_t>(8 * (wave + WAVES * q)) * k));
+  }
+
+  auto stage_base = [&](auto st) -> unsigned char* {
+    if constexpr (decltype(st)::value == 0) return lds0;
+    else return lds1;
+  };
+  auto issue = [&](int64_t g, auto st) {
+    unsigned char* base = stage_base(st);
+    const unsigned char* ag = a_base + g * kGroup;
+    const unsigned char* wg = w_base + g * kGroup;
+#pragma unroll
+    for (int q = 0; q < A_CHUNKS; ++q) {
+      if constexpr (CLAMP)
+        dma16(ag, a_off[q], base + 1024 * (wave + WAVES * q));
+      else
+        dma16(a_chunk[q] + g * kGroup, a_off[0], base + 1024 * (wave + WAVES * q));
+    }
+#pragma unroll
+    for (int q = 0; q < W_CHUNKS; ++q) {
+      if constexpr (CLAMP)
+        dma16(wg, w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
+      else
+        dma16(w_chunk[q] + g * kGroup, w_off[0], base + BM * 128 + 1024 * (wave + WAVES * q));
+    }
+    if (copies_scales) dma4(uniform(sa_base + g), 4 * sa_off, base + (BM + BN) * 128 + 256 * wave);
+  };
+  auto frag = [&](const unsigned char* base, int r) -> v8i {
+    const int x = r & 7;
+    const v4u lo = *reinterpret_cast<const v4u*>(base + r * 128 + 16 * (quarter ^ x));
+    const v4u hi = *reinterpret_cast<const v4u*>(base + r * 128 + 16 * ((quarter + 4) ^ x));
+    return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+  auto a_frag = [&](auto st, int j) -> v8i { return frag(stage_base(st), TM * wave_m + 16 * j + lrow); };
+  auto a_scale = [&](auto st, int j) -> float {
+    return reinterpret_cast<const float*>(stage_base(st) + (BM + BN) * 128)[TM * wave_m + 16 * j + lrow];
+  };
+  auto w_frag = [&](auto st, int i) -> v8i { return frag(stage_base(st) + BM * 128, TN * wave_n + 16 * i + lrow); };
+
+  v4f acc[I][J];
+#pragma unroll
+  for (int i = 0; i < I; ++i)
+#pragma unroll
+    for (int j = 0; j < J; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  // Prologue: step 0's tiles land, then step 1's copies go out and step 0's
+  // fragments come in.
+  issue(0, S0{});
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  issue(groups > 1 ? 1 : 0, S1{});
+  v8i wf[I];
+#pragma unroll
+  for (int i = 0; i < I; ++i) wf[i] = w_frag(S0{}, i);
+  v8i af = a_frag(S0{}, 0);
+  float sa = a_scale(S0{}, 0);
+  float sw_lanes = sw_chunk(0);
+  float sw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw_lanes), 0));
+  // results of the previous token sub-tile awaiting their scale FMA (zeros
+  // before the first: adding 0 * 0 leaves the +0 running sums unchanged)
+  v4f p_prev[I];
+#pragma unroll
+  for (int i = 0; i < I; ++i) p_prev[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  float sc_prev = 0.f;
+
+  // MFMAs of token sub-tile j (fragment af, scale sc) while the FMAs of the
+  // previous sub-tile's results (into acc[.][jp]) retire one per MFMA;
+  // `between(i)` runs after MFMA i (used to refill the weight fragments).
+  auto mfma_row = [&](int jp, float sc, auto between) {
+    v4f p_cur[I];
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      p_cur[i] = mfma_16x16x128_e4m3(wf[i], af);
+      acc[i][jp][0] = fmaf(sc_prev, p_prev[i][0], acc[i][jp][0]);
+      acc[i][jp][1] = fmaf(sc_prev, p_prev[i][1], acc[i][jp][1]);
+      acc[i][jp][2] = fmaf(sc_prev, p_prev[i][2], acc[i][jp][2]);
+      acc[i][jp][3] = fmaf(sc_prev, p_prev[i][3], acc[i][jp][3]);
+      asm volatile("" : "+v"(acc[i][jp]));
+      between(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < I; ++i) p_prev[i] = p_cur[i];
+    sc_prev = sc;
+  };
+  auto nothing = [](int) {};
+
+  // Step g from stage st: sub-tiles 0 .. J - 2 with the next fragment in
+  // flight; sub-tile J - 1 either across the barrier into step g + 1 (its
+  // MFMAs hide the latency of step g + 1's first fragment reads) or, at the
+  // last step, as a final drain.
+  auto step = [&](int64_t g, auto st) {
+    constexpr int cur = decltype(st)::value;
+    using SN = std::integral_constant<int, cur ^ 1>;
+#pragma unroll
+    for (int j = 0; j < J - 1; ++j) {
+      const v8i af_n = a_frag(st, j + 1);
+      const float sa_n = a_scale(st, j + 1);
+      mfma_row((j + J - 1) % J, sa * sw, nothing);
+      af = af_n;
+      sa = sa_n;
+    }
+    if (g + 1 < groups) {
+      if (((g + 1) & 63) == 0) sw_lanes = sw_chunk(g + 1);
+      const float sw_n = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw_lanes),
+                                                                             static_cast<int>((g + 1) & 63)));
+      // every LDS read of this stage has completed and step g + 1's tiles
+      // have landed (own copies: vmcnt; everyone's: the barrier)
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      const int64_t g2 = g + 2 < groups ? g + 2 : groups - 1;
+      issue(g2, st);
+      const v8i af_n = a_frag(SN{}, 0);
+      const float sa_n = a_scale(SN{}, 0);
+      mfma_row(J - 2, sa * sw, [&](int i) { wf[i] = w_frag(SN{}, i); });
+      af = af_n;
+      sa = sa_n;
+      sw = sw_n;
+    } else {
+      mfma_row(J - 2, sa * sw, nothing);
+    }
+  };
+
+  for (int64_t g = 0; g < groups; g += 2) {
+    step(g, S0{});
+    if (g + 1 < groups) step(g + 1, S1{});
+  }
+  // last sub-tile's results
+#pragma unroll
+  for (int i = 0; i < I; ++i) {
+    acc[i][J - 1][0] = fmaf(sc_prev, p_prev[i][0], acc[i][J - 1][0]);
+    acc[i][J - 1][1] = fmaf(sc_prev, p_prev[i][1], acc[i][J - 1][1]);
+    acc[i][J - 1][2] = fmaf(sc_prev, p_prev[i][2], acc[i][J - 1][2]);
+    acc[i][J - 1][3] = fmaf(sc_prev, p_prev[i][3], acc[i][J - 1][3]);
+  }
+  // copies issued past the last step must land before the LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t m = m0 + TM * wave_m + 16 * j + lrow;
+    if (m >= m_rows || m < m_own) continue;
+#pragma unroll
+    for (int i = 0; i < I; ++i) {
+      const int64_t col = n0 + TN * wave_n + 16 * i + 4 * quarter;
+      unsigned short* dst = c + m * n + col;
+      const v4f v = acc[i][j];
+      if ((n & 3) == 0 && col + 3 < n) {
+        v2u packed;
+        packed[0] = pack_bf16x2(v[0], v[1]);
+        packed[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<v2u*>(dst) = packed;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (col + e < n) dst[e] = static_cast<unsigned short>(pack_bf16x2(v[e], 0.f) & 0xffffu);
+      }
+    }
+  }
+}
+
 }  // namespace fp8bq
