@@ -382,55 +382,72 @@ def m_sweep():
     return rows
 
 
+READ_GRIDS = (256, 512, 1024, 2048)
+
+
+def graph_us(launch, count):
+    """Median over three replays of a HIP graph of `count` back-to-back
+    launches (launch(i) enqueues the i-th), microseconds per launch. Graph
+    replays keep the host's launch rate (several microseconds per call
+    through Python) out of the figure."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        e1.synchronize()
+        runs.append(e0.elapsed_time(e1) * 1e3 / count)
+    del g
+    return sorted(runs)[1]
+
+
+def best_read_us(views, sink):
+    """Fastest streaming read (fp8bq_mb_read, twelve 16-byte loads in flight
+    per lane) of one buffer of `views` over the grid sizes READ_GRIDS, the
+    launches rotating over the views: (us per read, grid)."""
+    best = None
+    for grid in READ_GRIDS:
+        us = graph_us(lambda i: fp8bq.mb_read(views[i % len(views)], grid, sink), max(24, 2 * len(views)))
+        if best is None or us < best[0]:
+            best = (us, grid)
+    return best
+
+
 def ceilings():
     """What this GPU delivers, to read the roofline fractions against besides
-    the published peaks (the library's measurement kernels). Each figure is
-    a run of back-to-back launches captured in a HIP graph and replayed, so
-    that the host's launch rate (several microseconds per call through
-    Python) does not bound it:
+    the published peaks (the library's measurement kernels), each as HIP
+    graph replays (graph_us):
     - the streaming-read time of each transfer size the GEMM moves per call
       (the five shapes' bytes at M = 1, the vocabulary projection, 1 GiB):
-      256 workgroups of 512 threads, buffers rotating over >= 1 GiB;
+      the fastest of 256 .. 2048 workgroups of 512 threads, twelve loads in
+      flight per lane, buffers rotating over >= 1 GiB;
     - one empty launch of the decode kernels' grid (256 x 512): the fixed
       cost each call pays;
     - the FP8 16x16x128 MFMA rate of 1024 workgroups x 4 waves x 8
-      independent chains (the matrix-core peak at the clock this load runs).
-    The median of three replays is reported."""
+      independent chains (the matrix-core peak at the clock this load runs)."""
     dev = torch.device("cuda:0")
-
-    def graph_us(launch, count):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(count):
-                launch(i)
-        g.replay()
-        torch.cuda.synchronize()
-        runs = []
-        for _ in range(3):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            g.replay()
-            e1.record()
-            e1.synchronize()
-            runs.append(e0.elapsed_time(e1) * 1e3 / count)
-        del g
-        return sorted(runs)[1]
-
     sizes = [(f"({n}, {k}) at M=1", gemm_bytes(1, n, k)) for n, k in workloads.SHAPES]
     sizes += [("vocabulary projection (152064, 5120)", 152064 * 5120), ("1 GiB", 1 << 30)]
     pool = torch.empty(3 << 30, dtype=torch.uint8, device=dev)
     pool.random_(0, 256)
-    sink = torch.empty(256, dtype=torch.int32, device=dev)
+    sink = torch.empty(max(READ_GRIDS), dtype=torch.int32, device=dev)
     read = []
     for name, nbytes in sizes:
         nbytes = nbytes // 256 * 256
         copies = max(2, min(pool.numel() // nbytes, -(-(1 << 30) // nbytes) + 1))
         views = [pool[i * nbytes:(i + 1) * nbytes] for i in range(copies)]
-        us = graph_us(lambda i: fp8bq.mb_read(views[i % copies], 256, sink), max(24, 2 * copies))
-        read.append({"what": name, "bytes": nbytes, "us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
-                     "pct_of_8TBps": round(nbytes / us / 1e3 / 80, 1)})
-        print(f"bench: read {name} {nbytes} B: {us:.2f} us", file=sys.stderr, flush=True)
+        us, grid = best_read_us(views, sink)
+        read.append({"what": name, "bytes": nbytes, "us": round(us, 2), "grid": grid,
+                     "GBps": round(nbytes / us / 1e3, 1), "pct_of_8TBps": round(nbytes / us / 1e3 / 80, 1)})
+        print(f"bench: read {name} {nbytes} B: {us:.2f} us (grid {grid})", file=sys.stderr, flush=True)
     del pool, views
     torch.cuda.empty_cache()
     empty_us = graph_us(lambda i: fp8bq.mb_empty(256, 512), 500)
@@ -444,39 +461,156 @@ def ceilings():
                                     "frac_of_5000": round(flops / mfma_us / 1e6 / FP8_PEAK_TFLOPS, 4)}}
 
 
-def cpu_baseline(budget_s=20.0, rows=4096):
-    """The CPU oracle (numpy, fp64 GEMM) on a bounded sample: quantise the
-    activation and compute the GEMM for M = 1..8 against the first `rows`
-    weight rows of the same workload, repeated until about `budget_s` of CPU
-    work. Reports GB/s of algorithmic bytes, like the GPU figure."""
+PER_SHAPE_M = [1, 2, 3, 4, 5, 6, 7, 8, 16, 32, 64]
+
+
+def per_shape():
+    """The decode, verify and batch configurations on all five logged shapes
+    (page 2, section 8): fp8bq_gemm at M = 1..8, 16, 32, 64 and
+    fp8bq_gemm_fused at M = 1..8, 16, each as HIP graph replays of
+    back-to-back calls with the weights rotating over >= 1 GiB of copies (no
+    call finds its weight in the 256 MB Infinity Cache). Per call: us, GB/s
+    of algorithmic bytes, % of 8 TB/s, and % of the fastest streaming read of
+    the same weight bytes over the same rotating buffers (`read_us`). Per
+    shape: the no-cliff ratio max over M = 2..8 of t(M) / t(1)."""
+    dev = torch.device("cuda:0")
+    L = fp8bq.lib()
+    g = torch.Generator(device=dev)
+    mmax = max(PER_SHAPE_M)
+    sink = torch.empty(max(READ_GRIDS), dtype=torch.int32, device=dev)
+    out = []
+    for n, k in workloads.SHAPES:
+        copies = max(4, -(-(1 << 30) // (n * k)))
+        g.manual_seed(4242)
+        w32 = torch.randn((n, k), generator=g, device=dev, dtype=torch.float32).mul_(0.02)
+        wq0, ws0 = fp8bq.quant_weight(w32)
+        del w32
+        ws = [(wq0.clone(), ws0.clone()) for _ in range(copies)]  # distinct buffers, same contents
+        del wq0, ws0
+        a = workloads.activation(mmax, n, k).to(dev)
+        aq, as_ = fp8bq.quant_act(a)
+        c = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        read_us, read_grid = best_read_us([wq for wq, _ in ws], sink)
+        row = {"N": n, "K": k, "weight_copies": copies, "read_us": round(read_us, 2), "read_grid": read_grid,
+               "read_pct_of_8TBps": round(100 * n * k / (read_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+               "gemm": [], "fused": []}
+        for kind in ("gemm", "fused"):
+            for m in PER_SHAPE_M:
+                if kind == "fused" and m > 16:
+                    continue
+
+                def call(i):
+                    wq, wsc = ws[i % copies]
+                    s = torch.cuda.current_stream(dev).cuda_stream  # the capturing stream
+                    if kind == "gemm":
+                        st = L.fp8bq_gemm(m, n, k, aq.data_ptr(), as_.data_ptr(), wq.data_ptr(), wsc.data_ptr(),
+                                          c.data_ptr(), s)
+                    else:
+                        st = L.fp8bq_gemm_fused(m, n, k, a.data_ptr(), wq.data_ptr(), wsc.data_ptr(), c.data_ptr(), s)
+                    if st:
+                        raise fp8bq.Fp8bqError(f"fp8bq_{kind}", st)
+
+                us = graph_us(call, max(24, 2 * copies))
+                nbytes = gemm_bytes(m, n, k) if kind == "gemm" else bf16_act_bytes(m, n, k)
+                gbs = nbytes / (us * 1e-6) / 1e9
+                row[kind].append({"M": m, "us": round(us, 2), "GBps": round(gbs, 1),
+                                  "pct_of_8TBps": round(100 * gbs / HBM_PEAK_GBS, 1),
+                                  "pct_of_read": round(100 * read_us / us, 1)})
+            t = {r["M"]: r["us"] for r in row[kind]}
+            row[f"no_cliff_{kind}"] = round(max(t[m] for m in range(2, 9)) / t[1], 3)
+        print(f"bench: per-shape N={n} K={k}: read {read_us:.2f} us, gemm M=1 {row['gemm'][0]['us']} us, "
+              f"fused M=1 {row['fused'][0]['us']} us", file=sys.stderr, flush=True)
+        out.append(row)
+        del ws, a, aq, as_, c
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(rows=4096, runs=5):
+    """The CPU oracle (numpy, fp64 GEMM) on a bounded sample of the workload:
+    activation quantisation (quant_act_ref) and the GEMM (gemm_ref) for
+    M = 1..8 against the first `rows` weight rows of (N, K) = (17408, 5120),
+    the weight pre-quantised. One warm-up pass, then the median of `runs`
+    passes, with the host's threads (all cores this process may use, at most
+    the OMP_NUM_THREADS share when that is set) and with one thread. Also the
+    plain fp64 matmul alone on pre-dequantised operands (the oracle's
+    arithmetic without its decode and per-group loop). Reported in GB/s of the
+    same algorithmic bytes as the GPU figure, and as us per call scaled to the
+    full N."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
-    from oracle import gemm_ref, quant_act_ref, quant_weight_ref
+    from oracle import e4m3_decode, gemm_ref, quant_act_ref, quant_weight_ref
 
     cores = len(os.sched_getaffinity(0))
-    cores = min(cores, 16)  # the GPU box's CPU share
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        cores = min(cores, int(env))
+    blocks = [quant_weight_ref(workloads.weight_block(N, K, b)) for b in range(rows // 128)]
+    w_q = np.concatenate([q for q, _ in blocks])
+    w_s = np.concatenate([s for _, s in blocks])
+    acts = {m: workloads.activation(m, N, K) for m in MS}
+    sample_bytes = sum(bf16_act_bytes(m, rows, K) for m in MS)
+
+    def one_pass():
+        t0 = time.perf_counter()
+        for m in MS:
+            a_q, a_s = quant_act_ref(acts[m])
+            gemm_ref(a_q, a_s, w_q, w_s)
+        return time.perf_counter() - t0
+
+    def median_pass():
+        one_pass()
+        return float(np.median([one_pass() for _ in range(runs)]))
+
+    # the same sums with operands already decoded and scaled, one fp64 matmul per M
+    w_deq = e4m3_decode(w_q) * np.repeat(np.repeat(w_s.astype(np.float64), 128, axis=0)[:rows], 128, axis=1)
+    a_deq = {}
+    for m in MS:
+        a_q, a_s = quant_act_ref(acts[m])
+        a_deq[m] = e4m3_decode(a_q) * np.repeat(a_s.astype(np.float64), 128, axis=1)
+
+    def matmul_pass():
+        t0 = time.perf_counter()
+        for m in MS:
+            a_deq[m] @ w_deq.T
+        return time.perf_counter() - t0
+
     with threadpool_limits(limits=cores):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        blocks = [quant_weight_ref(workloads.weight_block(N, K, b)) for b in range(rows // 128)]
-        w_q = np.concatenate([q for q, _ in blocks])
-        w_s = np.concatenate([s for _, s in blocks])
-        acts = {m: workloads.activation(m, N, K) for m in MS}
-        passes, t_total, bytes_total = 0, 0.0, 0
-        while t_total < budget_s and passes < 100:
-            t0 = time.perf_counter()
-            for m in MS:
-                a_q, a_s = quant_act_ref(acts[m])
-                gemm_ref(a_q, a_s, w_q, w_s)
-            t_total += time.perf_counter() - t0
-            bytes_total += sum(bf16_act_bytes(m, rows, K) for m in MS)
-            passes += 1
+        t_all = median_pass()
+        matmul_pass()
+        t_mm = float(np.median([matmul_pass() for _ in range(runs)]))
+    with threadpool_limits(limits=1):
+        t_one = median_pass()
+    scale = N / rows  # calls over the full weight take N / rows times the sample
     return {
-        "value": round(bytes_total / t_total / 1e9, 4),
+        "value": round(sample_bytes / t_all / 1e9, 4),
         "unit": "GB/s",
         "cores": used,
         "kind": "oracle",
-        "sample": f"{passes} pass(es) of quant_act_ref + gemm_ref for M=1..8 on the first {rows} of {N} weight "
-                  f"rows (K={K}); {t_total:.1f} s",
+        "cpu_model": cpu_model(),
+        "sample": f"quant_act_ref + gemm_ref for M=1..8 on the first {rows} of {N} weight rows (K={K}); "
+                  f"median of {runs} passes after 1 warm-up",
+        "pass_s": round(t_all, 4),
+        "us_per_call_full_N": round(t_all / len(MS) * scale * 1e6, 1),
+        "one_thread": {"value": round(sample_bytes / t_one / 1e9, 4), "unit": "GB/s", "pass_s": round(t_one, 4),
+                       "us_per_call_full_N": round(t_one / len(MS) * scale * 1e6, 1)},
+        "matmul_only": {"what": "fp64 A_deq @ W_deq.T per M, operands pre-dequantised", "pass_s": round(t_mm, 4),
+                        "value": round(sample_bytes / t_mm / 1e9, 4), "unit": "GB/s",
+                        "us_per_call_full_N": round(t_mm / len(MS) * scale * 1e6, 1)},
     }
 
 
@@ -489,7 +623,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the M=3465 prefill GEMM timing")
     ap.add_argument("--no-two-stage", action="store_true", help="skip the two-stage vocabulary scoring timing")
-    ap.add_argument("--only", choices=("prefill", "two-stage"),
+    ap.add_argument("--no-per-shape", action="store_true",
+                    help="skip the all-shapes decode/verify/batch leg (M = 1..8, 16, 32, 64 on the five shapes)")
+    ap.add_argument("--only", choices=("prefill", "two-stage", "per-shape", "cpu"),
                     help="run only this leg and print its JSON line (for profiling one kernel family)")
     ap.add_argument("--m-sweep", action="store_true",
                     help="instead of the benchmark, time fp8bq_gemm over an M grid on the five shapes (one JSON line)")
@@ -506,6 +642,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "this path has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
+    if args.only == "cpu":  # the CPU oracle alone (no GPU needed)
+        print(json.dumps({"metric": "CPU oracle", "cpu_baseline": cpu_baseline()}), flush=True)
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -513,6 +652,10 @@ def main():
     if args.only == "two-stage":
         print(json.dumps({"metric": "two-stage vocabulary scoring us/call", "data": "synthetic",
                           "two_stage": two_stage(), "device": torch.cuda.get_device_name(0)}), flush=True)
+        return
+    if args.only == "per-shape":
+        print(json.dumps({"metric": "block-FP8 GEMM us/call, five shapes", "data": "synthetic",
+                          "per_shape": per_shape(), "device": torch.cuda.get_device_name(0)}), flush=True)
         return
     if args.only == "prefill":
         print(json.dumps({"metric": "prefill block-FP8 GEMM us/call", "data": "synthetic",
@@ -655,10 +798,13 @@ def main():
     if not args.no_prefill:
         print("bench: timing the prefill GEMMs", file=sys.stderr, flush=True)
         rec["prefill"] = prefill(plan)
+    del plan
+    torch.cuda.empty_cache()
+    if not args.no_per_shape:
+        print("bench: timing the five shapes at M = 1..8, 16, 32, 64", file=sys.stderr, flush=True)
+        rec["per_shape"] = per_shape()
     if not args.no_two_stage:
         print("bench: timing two-stage vocabulary scoring", file=sys.stderr, flush=True)
-        del plan
-        torch.cuda.empty_cache()
         rec["two_stage"] = two_stage()
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)

@@ -294,7 +294,7 @@ int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void *h
  * fp8bq_mb_read: streaming read of `bytes` bytes at `buf` (bytes % 16 == 0,
  *   buf 16-B aligned) by `grid` (1..65536) workgroups of 512 threads,
  *   consecutive lanes on consecutive 16-byte units, non-temporal loads,
- *   four in flight per lane. sink [grid] uint32 (out): the XOR of the
+ *   twelve in flight per lane. sink [grid] uint32 (out): the XOR of the
  *   32-bit words each workgroup read; XORed together they equal the XOR of
  *   every word of the buffer. bytes == 0 (buf may then be NULL) writes
  *   zeros.

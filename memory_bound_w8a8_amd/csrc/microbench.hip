@@ -21,23 +21,29 @@ __device__ __forceinline__ unsigned xor4(const v4u& v) { return v[0] ^ v[1] ^ v[
 
 // Streaming read of n16 16-byte units: consecutive lanes read consecutive
 // units (1 KB per wave instruction), a grid-wide stride between a lane's
-// units, four non-temporal loads in flight per lane per trip (the tail trips
-// take one at a time). Every lane XORs what it read; each workgroup writes
-// the XOR over its lanes to sink[blockIdx.x], which keeps the loads live and
-// lets a test check that every word was read exactly once.
+// units, twelve non-temporal loads in flight per lane per trip (lanes past
+// the end skip theirs, so a transfer smaller than twelve grid-strides still
+// has all of its loads in flight at once).
+// Every lane XORs what it read; each workgroup writes the XOR over its lanes
+// to sink[blockIdx.x], which keeps the loads live and lets a test check that
+// every word was read exactly once.
+constexpr int kReadBatch = 12;
+
 __global__ __launch_bounds__(512) void mb_read_kernel(const v4u* __restrict__ src, int64_t n16,
                                                       unsigned* __restrict__ sink) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 512;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * 512 + threadIdx.x;
   unsigned x = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const v4u a = __builtin_nontemporal_load(src + i);
-    const v4u b = __builtin_nontemporal_load(src + i + stride);
-    const v4u c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const v4u d = __builtin_nontemporal_load(src + i + 3 * stride);
-    x ^= xor4(a) ^ xor4(b) ^ xor4(c) ^ xor4(d);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 512 + threadIdx.x; i < n16; i += kReadBatch * stride) {
+    v4u v[kReadBatch];
+#pragma unroll
+    for (int u = 0; u < kReadBatch; ++u) {
+      const int64_t j = i + u * stride;
+      v[u] = v4u{0u, 0u, 0u, 0u};
+      if (j < n16) v[u] = __builtin_nontemporal_load(src + j);
+    }
+#pragma unroll
+    for (int u = 0; u < kReadBatch; ++u) x ^= xor4(v[u]);
   }
-  for (; i < n16; i += stride) x ^= xor4(__builtin_nontemporal_load(src + i));
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x ^= static_cast<unsigned>(__shfl_xor(static_cast<int>(x), o));
   __shared__ unsigned part[8];
