@@ -162,12 +162,15 @@ int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_f
  *
  *   C = fp8bq_gemm(fp8bq_quant_act(A_bf16), W_fp8, W_scales)
  *
- *   A_bf16   [M, K] bf16, read; 1 <= M <= 16
+ *   A_bf16   [M, K] bf16, read; 1 <= M <= 8
  *   W_fp8, W_scales as fp8bq_gemm; C_bf16 [M, N] bf16, written.
+ * Up to 8 tokens: every workgroup of the launch quantises the whole
+ * activation, which beyond 8 tokens no longer hides under the weight stream
+ * of the narrower weights (two launches are faster there).
  * The codes and scales formed inside are exactly those fp8bq_quant_act
  * writes, and C is bitwise the two-call result; they are not stored.
  * M == 0 or N == 0 is a quick return; K == 0 writes zeros. Errors: NULL
- * pointer; negative size; K % 128 != 0; M > 16; K > 9216 (more than 72
+ * pointer; negative size; K % 128 != 0; M > 8; K > 9216 (more than 72
  * groups); M*K, N*K or M*N > 2^40; A_bf16, W_fp8 or C_bf16 not 16-B aligned,
  * W_scales not 4-B aligned; device not gfx950.
  */

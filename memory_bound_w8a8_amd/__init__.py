@@ -220,7 +220,7 @@ def gemm_w8a16(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
 
 def gemm_fused(a: torch.Tensor, w_q, w_s, out=None) -> torch.Tensor:
     """Activation quantisation and block-FP8 GEMM in one launch: bf16 [M, K]
-    (M <= 16) -> bf16 [M, N], bitwise gemm(*quant_act(a), w_q, w_s)."""
+    (M <= 8) -> bf16 [M, N], bitwise gemm(*quant_act(a), w_q, w_s)."""
     w_q, m, n, k, out = _bf16_act_args(a, w_q, w_s, out)
     with torch.cuda.device(a.device):
         st = lib().fp8bq_gemm_fused(m, n, k, _ptr(a), _ptr(w_q), _ptr(w_s), _ptr(out), _stream(a))
@@ -320,9 +320,8 @@ def rescore(h: torch.Tensor, w: torch.Tensor, idx: torch.Tensor):
 
 
 # Largest token count whose coarse logits two_stage() takes from the fused
-# launch; beyond it, quantisation + GEMM (bitwise the same logits) measured
-# faster at the vocabulary size (V = 152064, K = 5120: 127 vs 131 us at
-# M = 9, 135 vs 144 at M = 16; the fused launch wins or ties up to 8).
+# launch (the fused entry point serves up to 8 tokens); beyond it,
+# quantisation + GEMM, bitwise the same logits.
 TWO_STAGE_FUSED_MAX_M = 8
 
 

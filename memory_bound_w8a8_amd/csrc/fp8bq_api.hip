@@ -15,7 +15,8 @@ constexpr int64_t kStreamMaxM = 64;              // streaming kernels serve 1..6
 constexpr int64_t kStreamSplitMaxM = 128;        // forced streaming path: 65..128 as two launches (64 + the rest)
 constexpr int64_t kTiledMaxK = int64_t(1) << 24; // tiled kernel: 32-bit offsets within a 256-row tile
 constexpr int kMaxDevices = 64;
-constexpr int64_t kSmallMaxM = 16;               // fused and weight-only paths: one 16-token tile
+constexpr int64_t kSmallMaxM = 16;               // weight-only path: one 16-token tile
+constexpr int64_t kFusedMaxM = 8;                // fused path: quantisation layouts for up to 8 tokens
 constexpr int64_t kSmallMaxK = 72 * 128;         // groups within their instance tables
 constexpr int64_t kTopkMaxK = 256;               // survivors per row
 constexpr int64_t kMaxIndex = (int64_t(1) << 31) - 1;  // vocabulary indices are int32
@@ -151,7 +152,7 @@ int fp8bq_gemm_fused(int64_t M, int64_t N, int64_t K, const void* A_bf16, const 
                      void* C_bf16, void* stream) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
   if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
-  if (M > kSmallMaxM || K > kSmallMaxK) return FP8BQ_ERR_SHAPE;
+  if (M > kFusedMaxM || K > kSmallMaxK) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_OK;
   if (C_bf16 == nullptr) return FP8BQ_ERR_NULL;
   if (!aligned(C_bf16, 16)) return FP8BQ_ERR_ALIGN;

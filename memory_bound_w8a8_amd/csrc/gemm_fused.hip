@@ -6,9 +6,13 @@
 // The launch shape follows from (N, K) as for fp8bq_gemm (rows_shape). M
 // selects the quantisation layout: 1, 2, 3..4 and 5..8 tokens spread each
 // group's values over the whole wave (TOK = 1, 2, 4, 8: 64 / TOK lanes per
-// token, 2 TOK values per lane) and exchange the codes through LDS; 9..16
-// tokens quantise in the MFMA operand layout directly. Every M inside a
-// class runs the same instruction stream.
+// token, 2 TOK values per lane) and exchange the codes through LDS. Every M
+// inside a class runs the same instruction stream. Up to 8 tokens only:
+// every workgroup quantises the whole activation (there is no memory shared
+// between workgroups to quantise it once), and at 9..16 tokens that work no
+// longer hides under the weight stream of the narrower logged weights
+// (N = 5120 .. 8192), where quantisation + GEMM as two launches measured
+// faster.
 #include <array>
 #include <string>
 #include <utility>
@@ -34,7 +38,6 @@ constexpr auto kFused1 = fused_table<1>(std::make_integer_sequence<int, kMaxTile
 constexpr auto kFused2 = fused_table<2>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kFused4 = fused_table<4>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kFused8 = fused_table<8>(std::make_integer_sequence<int, kMaxTiles>{});
-constexpr auto kFused16 = fused_table<16>(std::make_integer_sequence<int, kMaxTiles>{});
 
 }  // namespace
 
@@ -43,9 +46,9 @@ hipError_t launch_gemm_fused(int64_t m, int64_t n, int64_t k, const void* a, con
   const GemmArgs args{m, n, k, a, nullptr, wq, ws, c, stream};
   int64_t rows_per_wg;
   int tiles, gmax;
-  if (m < 1 || m > 16 || !rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) return hipErrorInvalidValue;
-  const auto& table = m == 1 ? kFused1 : m == 2 ? kFused2 : m <= 4 ? kFused4 : m <= 8 ? kFused8 : kFused16;
-  const int tok = m == 1 ? 1 : m == 2 ? 2 : m <= 4 ? 4 : m <= 8 ? 8 : 16;
+  if (m < 1 || m > 8 || !rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) return hipErrorInvalidValue;
+  const auto& table = m == 1 ? kFused1 : m == 2 ? kFused2 : m <= 4 ? kFused4 : kFused8;
+  const int tok = m == 1 ? 1 : m == 2 ? 2 : m <= 4 ? 4 : 8;
   dispatch_log("gemm_fused", m, n, k,
                ("gemm_rows_kernel MT=16 act=bf16 TOK=" + std::to_string(tok) + " TILES=" + std::to_string(tiles) +
                 " GMAX=" + std::to_string(gmax) + " rows/wg=" + std::to_string(rows_per_wg) +

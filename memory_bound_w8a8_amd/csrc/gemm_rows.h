@@ -54,49 +54,6 @@ enum ActForm : int {
   kActBf16 = 2,       // bf16 activation, quantised in the kernel
 };
 
-// Quantise one group of a lane's token inside the MFMA operand layout: the
-// lane holds bf16 elements 16 q .. 16 q + 15 and 64 + 16 q .. 64 + 16 q + 15
-// of the group (q = lane / 16, four 16-byte pieces); lanes l, l ^ 16, l ^ 32,
-// l ^ 48 hold the rest of the same token's group. Same rule as
-// quant_act_kernel: amax over the 128 values, s = amax / 448 (IEEE; 1 for
-// an all-zero group), code = RNE(clamp(x / s, +-448)). Returns the 32 codes
-// in operand byte order and sets the scale.
-//
-// The quotient is quotient_e4m3_range (device_common.h): equal in code to
-// the IEEE division x / s whenever amax >= 2^-96; below, the division.
-__device__ __forceinline__ v8i quant_group_operand(const v4u (&raw)[4], float* scale) {
-  float x[32];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      x[8 * i + 2 * w] = bf16_lo(raw[i][w]);
-      x[8 * i + 2 * w + 1] = bf16_hi(raw[i][w]);
-    }
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  const float s = group_scale(amax);
-  *scale = s;
-  v8i out;
-  if (amax >= 0x1p-96f) {
-    const float y = 1.0f / s;
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-      out[d] = static_cast<int>(encode4_e4m3(quotient_e4m3_range(x[4 * d], s, y), quotient_e4m3_range(x[4 * d + 1], s, y),
-                                             quotient_e4m3_range(x[4 * d + 2], s, y),
-                                             quotient_e4m3_range(x[4 * d + 3], s, y)));
-  } else {
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-      out[d] = static_cast<int>(encode4_e4m3(scaled_clamped(x[4 * d], s), scaled_clamped(x[4 * d + 1], s),
-                                             scaled_clamped(x[4 * d + 2], s), scaled_clamped(x[4 * d + 3], s)));
-  }
-  return out;
-}
-
 // Largest value of v over each aligned group of LPT lanes (a power of two,
 // 1..64), returned to every lane of the group; v are bit patterns of
 // non-negative floats, whose order as unsigned integers is their order as
@@ -130,7 +87,12 @@ __device__ __forceinline__ unsigned lane_group_umax(unsigned v) {
 // quantise 32 values, mostly copies of other lanes'): lane l holds bf16
 // values V (l % LPT) .. V (l % LPT) + V - 1 of token l / LPT (LPT = 64 / TOK
 // lanes per token, V = 2 TOK, raw[] as bf16 pairs). Same rule as
-// quant_group_operand. The codes go to the wave's LDS slot (row = token,
+// quant_act_kernel: amax over the 128 values, s = amax / 448 (IEEE; 1 for an
+// all-zero group), code = RNE(x / s), with the quotient of
+// quotient_e4m3_gemm (device_common.h): equal in code to the IEEE division
+// whenever amax >= 2^-96 (a -0 may come out +0, which no GEMM sum can see);
+// below, the division. The codes feed only the MFMA, so C is bitwise that of
+// fp8bq_quant_act + fp8bq_gemm. The codes go to the wave's LDS slot (row = token,
 // 16-byte piece c of a row at 8 row + (c ^ (row & 7))), and the lane gets
 // back its MFMA operand, token min(l % 16, m_rows - 1), and that token's
 // scale. Requires m_rows <= TOK.
@@ -155,9 +117,9 @@ __device__ __forceinline__ v8i quant_group_compact(const v4u (&raw)[2], int m_ro
   const float s = group_scale(amax);
   float q[V];
   if (amax >= 0x1p-96f) {
-    const float y = 1.0f / s;
+    const RecipPair y = recip_pair(s);
 #pragma unroll
-    for (int j = 0; j < V; ++j) q[j] = quotient_e4m3_range(x[j], s, y);
+    for (int j = 0; j < V; ++j) q[j] = quotient_e4m3_gemm(x[j], y);
   } else {
 #pragma unroll
     for (int j = 0; j < V; ++j) q[j] = scaled_clamped(x[j], s);
@@ -194,7 +156,7 @@ struct RowsKernel {
   static constexpr int kRing = PD + 1;       // chunk register buffers
   static constexpr int kStageSlots = 2;      // LDS transpose slots per wave
   static constexpr int kLdsBytes =
-      S * kStageSlots * 2048 + S * TILES * kMS * 1024 + (AF == kActBf16 && TOK < 16 ? S * 2048 : 0);
+      S * kStageSlots * 2048 + S * TILES * kMS * 1024 + (AF == kActBf16 ? S * 2048 : 0);
 };
 
 template <int MT, int S, int GMAX, int TILES, int PD, int AF, int TOK = 16>
@@ -207,10 +169,10 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
   using KC = RowsKernel<MT, S, GMAX, TILES, PD, AF, TOK>;
   constexpr bool LINES = AF == kActCodeLines;
   constexpr bool BF16 = AF == kActBf16;
-  // bf16 activation of at most TOK < 16 tokens: quantised in the wave-wide
+  // bf16 activation of at most TOK <= 8 tokens: quantised in the wave-wide
   // layout of quant_group_compact (m_rows <= TOK)
-  constexpr bool COMPACT = BF16 && TOK < 16;
-  static_assert(!BF16 || MT == 16, "in-kernel quantisation serves one 16-token tile");
+  constexpr bool COMPACT = BF16;
+  static_assert(!BF16 || (MT == 16 && TOK <= 8), "in-kernel quantisation serves up to 8 tokens");
   // Chunk order. Tile-major (all groups of tile 0, then tile 1, ...) keeps
   // one accumulator set but holds the activation of all the wave's groups
   // in registers for the whole kernel; group-major (all tiles of group 0,
@@ -263,15 +225,15 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
   //  - kActCodes: the operand directly (token 16 s + lane % 16, pieces
   //    quarter and quarter + 4). With few tokens the clamped rows coincide,
   //    an instruction touches few lines, and no transposes are needed.
-  //  - kActBf16: the bf16 values of those operand positions (`aq` then
-  //    points at bf16 data, `as` is unused), quantised into codes and a
-  //    scale at the group's first use (quant_group_operand).
+  //  - kActBf16: the bf16 activation (`aq` then points at bf16 data, `as`
+  //    is unused), spread over the wave and quantised into the operand and a
+  //    scale at the group's first use (quant_group_compact).
   v8i bv[GMAX][MS];
   float sa[GMAX][MS];
   // (kActBf16: loaded with the group's first weight chunk, PD chunks ahead
   // of its first use, in load_chunk below; group-major order uses a group
   // for TILES consecutive chunks, so only a few groups are ever live.)
-  v4u araw[BF16 ? GMAX : 1][COMPACT ? 2 : 4];
+  v4u araw[BF16 ? GMAX : 1][2];
   __shared__ v4u astage[COMPACT ? S : 1][128];
   const unsigned short* arow = nullptr;
   if constexpr (COMPACT) {
@@ -279,9 +241,6 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     int tok = lane / LPT;
     tok = tok < m_rows ? tok : m_rows - 1;
     arow = reinterpret_cast<const unsigned short*>(aq) + static_cast<int64_t>(tok) * k + (lane % LPT) * (2 * TOK);
-  } else if constexpr (BF16) {
-    const int tok = lrow < m_rows ? lrow : m_rows - 1;
-    arow = reinterpret_cast<const unsigned short*>(aq) + static_cast<int64_t>(tok) * k + 16 * quarter;
   }
   // Activation codes (and scales) of group u for every 16-token tile, as
   // whole lines (LINES) or as the operand directly.
@@ -349,22 +308,16 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
     if (GROUP_MAJOR && !BF16 && t == 0) load_act(u);
     if (BF16 && t == 0) {
       const unsigned short* p = arow + static_cast<int64_t>(g) * kGroup;
-      if constexpr (COMPACT) {  // 2 TOK bf16 values of one token
-        if constexpr (TOK == 1) {
-          araw[u][0][0] = *reinterpret_cast<const unsigned*>(p);
-        } else if constexpr (TOK == 2) {
-          const v2u d = *reinterpret_cast<const v2u*>(p);
-          araw[u][0][0] = d[0];
-          araw[u][0][1] = d[1];
-        } else {
-          araw[u][0] = *reinterpret_cast<const v4u*>(p);
-          if constexpr (TOK == 8) araw[u][1] = *reinterpret_cast<const v4u*>(p + 8);
-        }
+      // 2 TOK bf16 values of one token
+      if constexpr (TOK == 1) {
+        araw[u][0][0] = *reinterpret_cast<const unsigned*>(p);
+      } else if constexpr (TOK == 2) {
+        const v2u d = *reinterpret_cast<const v2u*>(p);
+        araw[u][0][0] = d[0];
+        araw[u][0][1] = d[1];
       } else {
         araw[u][0] = *reinterpret_cast<const v4u*>(p);
-        araw[u][1] = *reinterpret_cast<const v4u*>(p + 8);
-        araw[u][2] = *reinterpret_cast<const v4u*>(p + 64);
-        araw[u][3] = *reinterpret_cast<const v4u*>(p + 72);
+        if constexpr (TOK == 8) araw[u][1] = *reinterpret_cast<const v4u*>(p + 8);
       }
     }
     const int64_t off = static_cast<int64_t>(g) * kGroup + piece * 16;
@@ -419,13 +372,12 @@ __global__ __launch_bounds__(64 * S) void gemm_rows_kernel(int m_rows, int64_t n
 #pragma unroll
       for (int s = 0; s < MS; ++s) at[s] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    if (BF16 && t == 0) {  // first use of group u: quantise its activation
-      float scale;
-      if constexpr (COMPACT)
+    if constexpr (BF16) {
+      if (t == 0) {  // first use of group u: quantise its activation
+        float scale;
         bv[u][0] = quant_group_compact<TOK>(araw[u], m_rows, astage[wave], &scale);
-      else
-        bv[u][0] = quant_group_operand(araw[u], &scale);
-      sa[u][0] = u < gcnt ? scale : 0.f;  // a group past the range adds nothing
+        sa[u][0] = u < gcnt ? scale : 0.f;  // a group past the range adds nothing
+      }
     }
     if (LINES && t == 0) {  // first use of group u: its activation lines -> operand
 #pragma unroll

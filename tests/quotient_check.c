@@ -30,6 +30,15 @@
  * the check skips the correction step (q = q0), which must then report code
  * mismatches: the check can fail.
  *
+ * The same run checks the quotient the fused GEMM uses instead (its codes
+ * feed only the MFMA, so the sign of a zero code does not matter there):
+ * y_hi = RN(1 / s), y_lo = RN(RN(1 - s y_hi) y_hi) once per group and
+ * q = fma(x, y_hi, RN(x y_lo)) per value, without a clamp. Its code must
+ * equal the division's for every x != 0 (x = +-0 may give either zero), and
+ * |q| must stay <= 448 (1 + 2^-23), where the hardware conversion still
+ * rounds to 448 (it gives the NaN code only above 464). Printed as
+ * gemm_code_differs, gemm_zero_sign_differs and gemm_qmax_over.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off quotient_check.c -lm
  */
 #include <math.h>
@@ -62,6 +71,8 @@ static unsigned e4m3_code(float v) {
 }
 
 static float clamp448(float q) { return fminf(fmaxf(q, -448.0f), 448.0f); }
+/* e4m3_code() of magnitudes in (448, 464] gives 0x7E, as the conversion
+   instruction does (ties at 464 go to the even code, 448). */
 
 int main(int argc, char** argv) {
   if (argc > 1 && strcmp(argv[1], "encode") == 0) {
@@ -75,11 +86,14 @@ int main(int argc, char** argv) {
   const uint32_t first_amax = 31u << 7; /* bf16 exponent field 31: 2^-96 */
   const uint32_t last_amax = 0x7F7Fu;   /* largest finite bf16 */
   unsigned long long pairs = 0, quot_diff = 0, code_diff = 0;
-#pragma omp parallel for schedule(dynamic, 64) reduction(+ : pairs, quot_diff, code_diff)
+  unsigned long long g_code_diff = 0, g_zero_sign = 0, g_over = 0;
+  const float qbound = 448.0f * (1.0f + 0x1p-23f);
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : pairs, quot_diff, code_diff, g_code_diff, g_zero_sign, g_over)
   for (uint32_t pa = first_amax; pa <= last_amax; ++pa) {
     const float amax = bf16_value(pa);
     const float s = amax / 448.0f;
     const float y = 1.0f / s;
+    const float y_lo = fmaf(-s, y, 1.0f) * y;
     const int with_negative = (pa % 17u) == 0;
     for (uint32_t px = 0; px <= pa; ++px) {
       for (int neg = 0; neg <= with_negative; ++neg) {
@@ -94,6 +108,12 @@ int main(int argc, char** argv) {
 #endif
         ++pairs;
         if (memcmp(&q_div, &q_fma, sizeof q_div) != 0) ++quot_diff;
+        const float q_gemm = fmaf(x, y, x * y_lo);
+        if (fabsf(q_gemm) > qbound) ++g_over;
+        if (e4m3_code(clamp448(q_div)) != e4m3_code(q_gemm)) {
+          if (x == 0.0f) ++g_zero_sign;
+          else ++g_code_diff;
+        }
         if (e4m3_code(clamp448(q_div)) != e4m3_code(clamp448(q_fma))) {
           ++code_diff;
 #ifndef UNCORRECTED
@@ -104,6 +124,8 @@ int main(int argc, char** argv) {
       }
     }
   }
-  printf("pairs %llu quotient_differs %llu code_differs %llu\n", pairs, quot_diff, code_diff);
-  return code_diff == 0 ? 0 : 1;
+  printf("pairs %llu quotient_differs %llu code_differs %llu gemm_code_differs %llu gemm_zero_sign_differs %llu "
+         "gemm_qmax_over %llu\n",
+         pairs, quot_diff, code_diff, g_code_diff, g_zero_sign, g_over);
+  return code_diff == 0 && g_code_diff == 0 && g_over == 0 ? 0 : 1;
 }

@@ -33,8 +33,8 @@ def _weights(n, k):
     return quant_weight_ref(workloads.weight(n, k))
 
 
-# every quantisation layout: 1, 2, 3..4, 5..8 tokens (compact) and 9..16
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16])
+# every quantisation layout: 1, 2, 3..4 and 5..8 tokens
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("n,k", [(640, 1024), (700, 384), (130, 1152), (4100, 2304), (1000, 9216)])
 def test_fused_bitwise_equals_two_calls(m, n, k):
     w_q, w_s = _weights(n, k)
@@ -75,14 +75,14 @@ def _adversarial(m, k, seed):
     return torch.from_numpy(x).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 5, 8])
 def test_fused_bitwise_adversarial(m):
     n, k = 520, 2048
     w_q, w_s = _weights(n, k)
     _check_bitwise(_adversarial(m, k, 100 + m), w_q, w_s, f"adversarial M={m}")
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_fused_bitwise_random_bf16_bit_patterns(seed, m):
     n, k = 300, 3072
@@ -107,7 +107,7 @@ def test_fused_against_oracle():
 @pytest.mark.parametrize("n,k", workloads.SHAPES)
 def test_fused_full_size_bitwise(n, k):
     w_q, w_s = fp8bq.quant_weight(to_gpu(workloads.weight(n, k)))
-    for m in (1, 2, 4, 8, 16):
+    for m in (1, 2, 3, 4, 5, 8):
         a_gpu = to_gpu(workloads.activation(m, n, k))
         ref = _two_call(a_gpu, w_q, w_s)
         got = fp8bq.gemm_fused(a_gpu, w_q, w_s)
@@ -115,7 +115,8 @@ def test_fused_full_size_bitwise(n, k):
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"M={m} N={n} K={k}"
 
 
-def test_fused_rejects_more_than_16_tokens():
+def test_fused_rejects_more_than_8_tokens():
     w_q, w_s = _weights(256, 256)
-    with pytest.raises(fp8bq.Fp8bqError):
-        fp8bq.gemm_fused(to_gpu(workloads.activation(17, 256, 256)), to_gpu(w_q), to_gpu(w_s))
+    for m in (9, 16, 17):
+        with pytest.raises(fp8bq.Fp8bqError):
+            fp8bq.gemm_fused(to_gpu(workloads.activation(m, 256, 256)), to_gpu(w_q), to_gpu(w_s))

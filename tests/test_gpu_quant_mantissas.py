@@ -1,8 +1,9 @@
 """GPU parity of the in-kernel quotient over every bf16 amax mantissa.
 
 The quantisation kernels form x / s from a reciprocal and one fma
-correction (IEEE division only below amax = 2^-96), so bit-exactness depends
-on the (x, amax) pair. These tests take every one of the 128 mantissa
+correction (fp8bq_quant_act) or from a two-term reciprocal (the quantisation
+inside fp8bq_gemm_fused), with the IEEE division only below amax = 2^-96,
+so bit-exactness depends on the (x, amax) pair. These tests take every one of the 128 mantissa
 patterns of the group maximum at 29 exponent fields -- bf16 subnormal
 maxima, maxima whose scale amax / 448 is an fp32 subnormal, the 2^-104 ..
 2^-96 neighbourhood of the switch to division, and normal maxima up to the
@@ -11,7 +12,7 @@ a * 2^-19 <= |x| <= a of both signs (everything that quantises to a non-zero
 code, and the first values that round to zero).
 
 * fp8bq_quant_act: codes and scales bit-exact against quant_act_ref.
-* fp8bq_gemm_fused, every quantisation layout (1, 2, 3..4, 5..8 and 9..16
+* fp8bq_gemm_fused, every quantisation layout (1, 2, 3..4 and 5..8
   tokens): against an identity weight (N = K, code 1.0 on the diagonal) the
   GEMM definition reduces to C[m, n] = dec(q[m, n]) * s[m, g] * sw[g, g]
   (g = n / 128), with one fp32 rounding of that exact product (the kernel's
@@ -113,7 +114,7 @@ def _block_scale_exponent(amax_bits: np.ndarray) -> np.ndarray:
     return np.clip(1 - ex, -100, 127)
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
 def test_fused_every_amax_mantissa_identity_weight(m):
     groups, owner, maxima = _mantissa_band()
     oq, os_ = _oracle_band()

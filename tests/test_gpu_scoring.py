@@ -227,7 +227,7 @@ def test_coarse_logits_vocabulary_size_sampled():
     ws_cat = np.concatenate([os_ for _, os_ in ow])
     cols_local = np.concatenate([128 * i + np.arange(oq.shape[0]) for i, (oq, _) in enumerate(ow)])
     cols_global = np.concatenate([128 * b + np.arange(oq.shape[0]) for b, (oq, _) in zip(blocks, ow)])
-    for m in (1, 4, 16):
+    for m in (1, 4, 8):
         h = workloads.activation(m, v, kdim)
         logits = fp8bq.gemm_fused(to_gpu(h), w_q, w_s)
         torch.cuda.synchronize()

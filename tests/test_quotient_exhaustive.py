@@ -1,12 +1,14 @@
-"""Exhaustive CPU check of the quotient the quantisation kernels use.
+"""Exhaustive CPU check of the quotients the quantisation kernels use.
 
 The kernels (activation quantisation and the quantisation fused into the
 GEMM) form x / s as a correctly rounded reciprocal of s followed by one
 fma-based correction (Markstein's method) instead of an IEEE division per
-value, for every group whose amax is at least 2^-96. `quotient_check.c`
-runs that sequence in host fp32 (libm's correctly rounded fmaf) for every
-bf16 amax >= 2^-96 and every bf16 x in [0, amax], clamps to +-448 and rounds
-both quotients to e4m3, and counts code mismatches, which must be zero.
+value, for every group whose amax is at least 2^-96; the quantisation inside
+the fused GEMM uses a two-term reciprocal instead (two operations per value,
+no clamp). `quotient_check.c` runs both in host fp32 (libm's correctly
+rounded fmaf) for every bf16 amax >= 2^-96 and every bf16 x in [0, amax],
+rounds them to e4m3 and counts code mismatches against the IEEE division,
+which must be zero (for the fused form: except the sign of a zero).
 
 The harness's own e4m3 rounding is pinned to the oracle's encoder on the
 codec's critical points, and a build without the correction step must
@@ -73,6 +75,10 @@ def test_corrected_quotient_gives_division_codes_for_every_bf16_pair(tmp_path):
     rc, stats, err = _run_check(_build(tmp_path))
     assert stats["pairs"] == _expected_pairs()
     assert stats["code_differs"] == 0, err[:2000]
+    # the fused GEMM's two-term-reciprocal quotient: same codes except the
+    # sign of a zero, never above 448 (1 + 2^-23)
+    assert stats["gemm_code_differs"] == 0
+    assert stats["gemm_qmax_over"] == 0
     assert rc == 0
     # the quotients themselves do differ sometimes: the code, not the fp32
     # value, is what the check establishes
