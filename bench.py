@@ -385,11 +385,38 @@ def m_sweep():
 READ_GRIDS = (256, 512, 1024, 2048)
 
 
+# Set by --launch-loop: graph_us times plain launch loops instead of graph
+# replays (for profilers that count per kernel dispatch).
+LAUNCH_LOOP = False
+
+
+def loop_us(launch, count):
+    """Median over three event-timed windows of `count` back-to-back direct
+    launches after one untimed window, microseconds per launch (includes
+    the host's launch rate wherever a call is shorter than its launch)."""
+    stream = torch.cuda.current_stream()
+    for i in range(count):
+        launch(i)
+    runs = []
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(count):
+            launch(i)
+        e1.record(stream)
+        e1.synchronize()
+        runs.append(e0.elapsed_time(e1) * 1e3 / count)
+    return sorted(runs)[1]
+
+
 def graph_us(launch, count):
     """Median over three replays of a HIP graph of `count` back-to-back
     launches (launch(i) enqueues the i-th), microseconds per launch. Graph
     replays keep the host's launch rate (several microseconds per call
-    through Python) out of the figure."""
+    through Python) out of the figure. With LAUNCH_LOOP set: loop_us."""
+    if LAUNCH_LOOP:
+        return loop_us(launch, count)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(count):
@@ -464,8 +491,9 @@ def ceilings():
 PER_SHAPE_M = [1, 2, 3, 4, 5, 6, 7, 8, 16, 32, 64]
 
 
-def per_shape():
+def per_shape(shapes=None):
     """The decode, verify and batch configurations on all five logged shapes
+    (or the (N, K) pairs in `shapes`)
     (page 2, section 8): fp8bq_gemm at M = 1..8, 16, 32, 64 and
     fp8bq_gemm_fused at M = 1..8, each as HIP graph replays of
     back-to-back calls with the weights rotating over >= 1 GiB of copies (no
@@ -479,7 +507,7 @@ def per_shape():
     mmax = max(PER_SHAPE_M)
     sink = torch.empty(max(READ_GRIDS), dtype=torch.int32, device=dev)
     out = []
-    for n, k in workloads.SHAPES:
+    for n, k in shapes or workloads.SHAPES:
         copies = max(4, -(-(1 << 30) // (n * k)))
         g.manual_seed(4242)
         w32 = torch.randn((n, k), generator=g, device=dev, dtype=torch.float32).mul_(0.02)
@@ -632,10 +660,22 @@ def main():
     ap.add_argument("--ceilings", action="store_true",
                     help="instead of the benchmark, measure the streaming-read, launch and FP8 MFMA ceilings "
                          "(one JSON line)")
+    ap.add_argument("--shape", action="append", default=[], metavar="N,K",
+                    help="per-shape leg: only this weight shape (repeatable; default: the five logged shapes)")
+    ap.add_argument("--launch-loop", action="store_true",
+                    help="per-shape leg and ceilings: time event-bracketed launch loops instead of HIP graph "
+                         "replays (for rocprofv3 counter runs, which count per dispatch)")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a dispatch of known traffic for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
+
+    global LAUNCH_LOOP
+    LAUNCH_LOOP = args.launch_loop
+    shapes = [tuple(int(x) for x in sh.split(",")) for sh in args.shape] or None
+    if shapes and any(sh not in workloads.SHAPES for sh in shapes):
+        print(f"--shape must name one of the logged shapes {workloads.SHAPES}", file=sys.stderr)
+        sys.exit(2)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -649,13 +689,24 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibration_copy_mb > 0:
+        nbytes = args.calibration_copy_mb << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"bench: calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
+
     if args.only == "two-stage":
         print(json.dumps({"metric": "two-stage vocabulary scoring us/call", "data": "synthetic",
                           "two_stage": two_stage(), "device": torch.cuda.get_device_name(0)}), flush=True)
         return
     if args.only == "per-shape":
         print(json.dumps({"metric": "block-FP8 GEMM us/call, five shapes", "data": "synthetic",
-                          "per_shape": per_shape(), "device": torch.cuda.get_device_name(0)}), flush=True)
+                          "per_shape": per_shape(shapes), "device": torch.cuda.get_device_name(0)}), flush=True)
         return
     if args.only == "prefill":
         print(json.dumps({"metric": "prefill block-FP8 GEMM us/call", "data": "synthetic",
@@ -671,16 +722,6 @@ def main():
         print(json.dumps({"metric": "fp8bq_gemm us/call over M", "data": "synthetic", "rows": m_sweep(),
                           "device": torch.cuda.get_device_name(0)}), flush=True)
         return
-
-    if args.calibration_copy_mb > 0:
-        nbytes = args.calibration_copy_mb << 20
-        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"bench: calibration copy of {nbytes} bytes done", file=sys.stderr, flush=True)
-        del src, dst
 
     w_bytes = N * K
     copies = max(4, -(-(1 << 30) // w_bytes))  # >= 1 GiB of distinct weights

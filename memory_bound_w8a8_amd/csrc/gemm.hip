@@ -166,20 +166,47 @@ hipError_t tiled_instance(int64_t m, int64_t n, int64_t k, const void* aq, const
 // The 8-wave two-stage tiles (192 x 256, 256 x 256): gemm_tiled2_kernel,
 // unclamped when every row of every tile exists once the last token tile is
 // shifted back (M >= BM, N a multiple of BN, a tile's rows within 32-bit
-// copy offsets).
+// copy offsets). A last round of at most 128 tiles after whole rounds (e.g. M = 3465 on
+// (5120, 8704): 380 tiles of 192 x 256 = 256 + 124) runs as a second launch
+// of column halves, 2 x 124 workgroups of 192 x 128 in one round at about
+// half a round's time, instead of 124 whole tiles leaving half the CUs idle.
+template <int BM, int BN, bool CLAMP>
+void tiled2_launch(int64_t m, int64_t n, int64_t k, int64_t t0, int split, int64_t grid, const void* aq,
+                   const float* as, const void* wq, const float* ws, void* c, hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_tiled2_kernel<BM, BN, 2, 4, CLAMP>), dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream,
+                     m, n, k, t0, split, static_cast<const unsigned char*>(aq), as,
+                     static_cast<const unsigned char*>(wq), ws, static_cast<unsigned short*>(c));
+}
+
+template <int BM, int BN>
+struct Tiled2Plan {
+  int64_t tiles, whole, halves;  // tiles of BM x BN; whole tiles launched first; then column halves
+  Tiled2Plan(int64_t m, int64_t n) {
+    tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    const int64_t rem = tiles % kNumCUs;
+    const bool split = tiles > kNumCUs && rem > 0 && 2 * rem <= kNumCUs;
+    whole = split ? tiles - rem : tiles;
+    halves = split ? 2 * rem : 0;
+  }
+};
+
 template <int BM, int BN>
 hipError_t tiled2_instance(int64_t m, int64_t n, int64_t k, const void* aq, const float* as, const void* wq,
                            const float* ws, void* c, hipStream_t stream) {
-  const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const Tiled2Plan<BM, BN> plan(m, n);
   const bool exact = m >= BM && n % BN == 0 && k < (int64_t(1) << 23);
-  if (exact)
-    hipLaunchKernelGGL((gemm_tiled2_kernel<BM, BN, 2, 4, false>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0,
-                       stream, m, n, k, static_cast<const unsigned char*>(aq), as, static_cast<const unsigned char*>(wq),
-                       ws, static_cast<unsigned short*>(c));
-  else
-    hipLaunchKernelGGL((gemm_tiled2_kernel<BM, BN, 2, 4, true>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0,
-                       stream, m, n, k, static_cast<const unsigned char*>(aq), as, static_cast<const unsigned char*>(wq),
-                       ws, static_cast<unsigned short*>(c));
+  if (plan.whole > 0) {
+    if (exact)
+      tiled2_launch<BM, BN, false>(m, n, k, 0, 1, plan.whole, aq, as, wq, ws, c, stream);
+    else
+      tiled2_launch<BM, BN, true>(m, n, k, 0, 1, plan.whole, aq, as, wq, ws, c, stream);
+  }
+  if (plan.halves > 0) {
+    if (exact)
+      tiled2_launch<BM, BN / 2, false>(m, n, k, plan.whole, 2, plan.halves, aq, as, wq, ws, c, stream);
+    else
+      tiled2_launch<BM, BN / 2, true>(m, n, k, plan.whole, 2, plan.halves, aq, as, wq, ws, c, stream);
+  }
   return hipGetLastError();
 }
 
@@ -194,14 +221,16 @@ struct TileShape {
   // tiles)
   int step_cost, step_cost2;
   const char* desc;
+  bool halves_last = false;  // 8-wave tiles: a last round of <= 128 tiles as column halves
+  int step_cost_halves = 0;  // ... at this measured cost (1/100 us per K step)
 };
 // Indexed as the forced tile-shape paths of fp8bq_gemm_forced (0..6 =
 // FP8BQ_PATH_TILED_128x128 .. FP8BQ_PATH_TILED_64x64).
 constexpr TileShape kTileShapes[] = {
     {128, 128, 1, 85, 85, "gemm_tiled_kernel BM=128 BN=128 4 waves 3 stages"},
     {128, 256, 1, 115, 115, "gemm_tiled_kernel BM=128 BN=256 8 waves 3 stages"},
-    {192, 256, 1, 150, 150, "gemm_tiled2_kernel BM=192 BN=256 8 waves 2 stages"},
-    {256, 256, 1, 190, 190, "gemm_tiled2_kernel BM=256 BN=256 8 waves 2 stages"},
+    {192, 256, 1, 150, 150, "gemm_tiled2_kernel BM=192 BN=256 8 waves 2 stages", true, 126},
+    {256, 256, 1, 190, 190, "gemm_tiled2_kernel BM=256 BN=256 8 waves 2 stages", true, 160},
     {64, 128, 2, 60, 100, "gemm_tiled_kernel BM=64 BN=128 4 waves 3 stages"},
     {128, 64, 2, 60, 100, "gemm_tiled_kernel BM=128 BN=64 4 waves 3 stages"},
     {64, 64, 3, 52, 90, "gemm_tiled_kernel BM=64 BN=64 4 waves 3 stages"},
@@ -228,6 +257,10 @@ int64_t tile_count(int64_t m, int64_t n, const TileShape& t) { return ((m + t.bm
 //    tiles and 48 streaming the weights twice). Once their grid outgrows
 //    one workgroup per CU the smaller tiles lose their edge (64 x 64 at
 //    M = 192 on N = 8192: 35 us against 26 for 128 x 64).
+//  - The 8-wave tiles run a last round of at most 128 tiles (after whole
+//    rounds) as column halves, which measured 0.84 of a whole round (a half
+//    tile's K step is bound by its copies' latency more than by its MFMAs):
+//    M = 3465 on (5120, 8704), 380 tiles of 192 x 256, 189 -> 173 us.
 // Equal costs go to the grid with more tiles (the better-filled machine),
 // then to the earlier shape in the order 64x64, 64x128, 128x64, 128x128,
 // 128x256, 192x256, 256x256.
@@ -240,7 +273,11 @@ int tiled_shape(int64_t m, int64_t n) {
     const int64_t tiles = tile_count(m, n, t);
     const int64_t cap = static_cast<int64_t>(kNumCUs) * t.per_cu;
     const int64_t rounds = (tiles + cap - 1) / cap;
-    const int64_t cost = rounds * (tiles > kNumCUs ? t.step_cost2 : t.step_cost);
+    int64_t cost = rounds * (tiles > kNumCUs ? t.step_cost2 : t.step_cost);
+    if (t.halves_last) {  // a last round of <= 128 tiles runs as column halves
+      const int64_t rem = tiles % kNumCUs;
+      if (tiles > kNumCUs && rem > 0 && 2 * rem <= kNumCUs) cost = (rounds - 1) * t.step_cost + t.step_cost_halves;
+    }
     if (cost < best_cost || (cost == best_cost && tiles > best_tiles)) {
       best = i;
       best_cost = cost;
@@ -254,9 +291,14 @@ hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, co
                              const void* wq, const float* ws, void* c, hipStream_t stream, int shape) {
   if (shape < 0) shape = tiled_shape(m, n);
   if (shape >= kNumTileShapes) return hipErrorInvalidValue;
-  dispatch_log("gemm(tiled)", m, n, k,
-               (std::string(kTileShapes[shape].desc) + " grid=" + std::to_string(tile_count(m, n, kTileShapes[shape])))
-                   .c_str());
+  std::string desc = std::string(kTileShapes[shape].desc) + " grid=" + std::to_string(tile_count(m, n, kTileShapes[shape]));
+  if (shape == 2 || shape == 3) {
+    const int64_t whole = shape == 2 ? Tiled2Plan<192, 256>(m, n).whole : Tiled2Plan<256, 256>(m, n).whole;
+    const int64_t halves = shape == 2 ? Tiled2Plan<192, 256>(m, n).halves : Tiled2Plan<256, 256>(m, n).halves;
+    if (halves > 0)
+      desc += " (" + std::to_string(whole) + " whole + " + std::to_string(halves) + " column halves)";
+  }
+  dispatch_log("gemm(tiled)", m, n, k, desc.c_str());
   switch (shape) {
     case 0:
       return tiled_instance<128, 128, 2, 2, 3>(m, n, k, aq, as, wq, ws, c, stream);

@@ -387,9 +387,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
 //    only the rows the previous tile does not, so no row is clamped and one
 //    lane offset serves every copy. CLAMP = true keeps the per-chunk clamped
 //    offsets of gemm_tiled_kernel.
+//  - A launch covers the tiles t0 .. t0 + gridDim.x / split - 1 of the grid of
+//    BM x (split BN) tiles, each as `split` workgroups of BN columns (split
+//    = 1: whole tiles; split = 2: the two column halves of a tile, so that a
+//    last, partly filled round of whole tiles can run as one round of
+//    halves, each output still summed over its groups in the same order).
 template <int BM, int BN, int WM, int WN, bool CLAMP>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_rows, int64_t n, int64_t k,
-                                                                   const unsigned char* __restrict__ aq,
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_rows, int64_t n, int64_t k, int64_t t0,
+                                                                   int split, const unsigned char* __restrict__ aq,
                                                                    const float* __restrict__ as,
                                                                    const unsigned char* __restrict__ wq,
                                                                    const float* __restrict__ ws,
@@ -413,13 +418,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
   const int64_t groups = k >> 7;
 
   const int64_t m_tiles = (m_rows + BM - 1) / BM;
-  const int64_t n_tiles = (n + BN - 1) / BN;
+  const int64_t n_tiles = (n + split * BN - 1) / (split * BN);  // tiles of split * BN columns
   int64_t tm, tn;
-  band_tile(xcd_tile(blockIdx.x, m_tiles * n_tiles), m_tiles, n_tiles, 8, &tm, &tn);
+  const int64_t u = xcd_tile(blockIdx.x, gridDim.x);
+  band_tile(t0 + u / split, m_tiles, n_tiles, 8, &tm, &tn);
   const int64_t m_own = tm * BM;  // first token row this tile stores
   int64_t m0 = m_own;
   if (!CLAMP && m0 + BM > m_rows) m0 = m_rows - BM;  // last token tile shifted back: every row valid
-  const int64_t n0 = tn * BN;
+  const int64_t n0 = (tn * split + u % split) * BN;
+  if (n0 >= n) return;  // a column half wholly past N (whole workgroup, before any barrier)
 
   constexpr int A_CHUNKS = BM / 8 / WAVES;
   constexpr int W_CHUNKS = BN / 8 / WAVES;

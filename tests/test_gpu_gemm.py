@@ -163,6 +163,27 @@ def test_tile_shapes_whole_output_and_bitwise(m, n, k):
         assert torch.equal(c.view(torch.int16), outs[0].view(torch.int16)), f"tile path {path}"
 
 
+# Grids of the 8-wave tiles with a last round of at most 128 tiles run that
+# round as column halves (a second launch of BM x BN/2 workgroups): whole
+# output against the oracle and bitwise equal to 128 x 128 tiles, for the
+# exact (N a multiple of BN) and the clamped kernel, including a column half
+# wholly past N (N = 8000: the last 256-column tile's second half starts at
+# 8064).
+@pytest.mark.parametrize("m,n,k,path", [(2000, 8000, 256, fp8bq.PATH_TILED_192x256),
+                                        (2100, 8000, 256, fp8bq.PATH_TILED_256x256),
+                                        (2000, 8192, 256, fp8bq.PATH_TILED_192x256),
+                                        (2100, 8192, 384, fp8bq.PATH_TILED_256x256)])
+def test_tiled2_last_round_column_halves(m, n, k, path):
+    a_q, a_s, w_q, w_s = _problem(m, n, k)
+    ref = gemm_ref(a_q, a_s, w_q, w_s)
+    args = [to_gpu(a_q), to_gpu(a_s), to_gpu(w_q), to_gpu(w_s)]
+    c = fp8bq.gemm_forced(path, *args)
+    c_128 = fp8bq.gemm_forced(fp8bq.PATH_TILED_128x128, *args)
+    torch.cuda.synchronize()
+    assert_gemm_close(bf16_to_f64(c), ref, what=f"tile path {path} M={m} N={n} K={k}")
+    assert torch.equal(c.view(torch.int16), c_128.view(torch.int16))
+
+
 def test_deterministic_repeat_calls():
     a_q, a_s, w_q, w_s = _problem(8, 5120, 3072)
     args = [to_gpu(a_q), to_gpu(a_s), to_gpu(w_q), to_gpu(w_s)]
