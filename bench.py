@@ -233,8 +233,46 @@ def prefill(plan, reps=20):
         us = sorted(windows)[1]
         tflops = 2.0 * m * n * k / (us * 1e-6) / 1e12
         out.append({"M": m, "N": n, "K": k, "us": round(us, 2), "us_windows": [round(w, 2) for w in windows],
-                    "TFLOPs": round(tflops, 1), "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)})
+                    "TFLOPs": round(tflops, 1), "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+                    "vendor_fp8_gemm_context": vendor_fp8_gemm(m, n, k, reps)})
+        del a, aq, as_, c
     return out
+
+
+def vendor_fp8_gemm(m, n, k, reps):
+    """For context only (not this library's path): the same (M, N, K) through
+    torch._scaled_mm on e4m3fn tensors with one scale per tensor (the ROCm
+    build routes it to hipBLASLt), i.e. an FP8 GEMM without the block scales'
+    per-group work, timed like prefill(). None where unsupported."""
+    dev = torch.device("cuda:0")
+    try:
+        g = torch.Generator(device=dev)
+        g.manual_seed(3)
+        a8 = torch.randn((m, k), generator=g, device=dev).mul_(100.0).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+        w8 = torch.randn((n, k), generator=g, device=dev).mul_(100.0).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
+        one = torch.ones((), device=dev)
+
+        def call():
+            return torch._scaled_mm(a8, w8.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+
+        for _ in range(reps):
+            call()
+        windows = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            e1.synchronize()
+            windows.append(e0.elapsed_time(e1) * 1e3 / reps)
+        us = sorted(windows)[1]
+        tflops = 2.0 * m * n * k / (us * 1e-6) / 1e12
+        return {"what": "torch._scaled_mm e4m3fn, per-tensor scales (hipBLASLt), no block scales", "us": round(us, 2),
+                "TFLOPs": round(tflops, 1), "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)}
+    except (RuntimeError, AttributeError, TypeError) as e:
+        return {"what": "torch._scaled_mm unsupported here", "error": str(e)[:200]}
 
 
 def two_stage(reps=50):
@@ -483,9 +521,21 @@ def ceilings():
     msink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
     mfma_us = graph_us(lambda i: fp8bq.mb_mfma(grid, iters, sink=msink), 3)
     flops = grid * 4 * 8 * iters * 2.0 * 16 * 16 * 128
+    # the same loop on quantised Gaussian operands (a GEMM's switching
+    # activity): the rate the power budget leaves a real FP8 GEMM
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    vals = torch.randn(fp8bq.MB_MFMA_DATA_BYTES, generator=g, device=dev).mul_(448.0 / 4.0)
+    codes = vals.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    data_us = graph_us(lambda i: fp8bq.mb_mfma_data(grid, iters, codes, sink=msink), 3)
+    print(f"bench: MFMA loop {flops / mfma_us / 1e6:.0f} TFLOP/s (one code), {flops / data_us / 1e6:.0f} "
+          "(Gaussian codes)", file=sys.stderr, flush=True)
     return {"read": read, "empty_launch_us": round(empty_us, 3),
             "mfma_e4m3_16x16x128": {"TFLOPs": round(flops / mfma_us / 1e6, 1), "us": round(mfma_us, 1),
-                                    "frac_of_5000": round(flops / mfma_us / 1e6 / FP8_PEAK_TFLOPS, 4)}}
+                                    "frac_of_5000": round(flops / mfma_us / 1e6 / FP8_PEAK_TFLOPS, 4)},
+            "mfma_e4m3_16x16x128_gaussian_codes": {
+                "TFLOPs": round(flops / data_us / 1e6, 1), "us": round(data_us, 1),
+                "frac_of_5000": round(flops / data_us / 1e6 / FP8_PEAK_TFLOPS, 4)}}
 
 
 PER_SHAPE_M = [1, 2, 3, 4, 5, 6, 7, 8, 16, 32, 64]

@@ -292,7 +292,7 @@ int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void *h
  * roofline fractions against besides the published peaks (page 1, SmartX
  * blog: "single-stream optimisation" reports bytes per decode step over time
  * against a calibrated bandwidth; "test background" calibrates the tools
- * first). All three only read their inputs and write `sink`.
+ * first). All four only read their inputs and write `sink`.
  *
  * fp8bq_mb_read: streaming read of `bytes` bytes at `buf` (bytes % 16 == 0,
  *   buf 16-B aligned) by `grid` (1..65536) workgroups of 512 threads,
@@ -309,11 +309,23 @@ int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void *h
  *   `code` (0..255, not a NaN code). sink [grid * 256] fp32 (out): thread t
  *   writes 4096 * iters * decode(code)^2 (exact while that fits in fp32's
  *   24 bits).
+ * fp8bq_mb_mfma_e4m3_data: the same loop with operands read from `codes`
+ *   (device, 16-B aligned, 32768 bytes of e4m3 codes, no NaN code; NaN codes
+ *   give unspecified sums): in every wave, chain u's first and second operand
+ *   in lane l are the 32 bytes at codes + 32 * ((2u + o) * 64 + l), o = 0, 1.
+ *   Output element i of lane l (row 4 (l / 16) + i, column l % 16) is
+ *   sum over q = 0..3, b = 0..31 of decode(first[16q + row][b]) *
+ *   decode(second[16q + column][b]) (lane L's bytes first[L][.], second[L][.]),
+ *   accumulated `iters` times in fp32; thread t writes the sum of its 32
+ *   elements (8 chains x 4) to sink[t] (sink [grid * 256] fp32). With
+ *   quantised Gaussian codes this is the matrix-core rate a GEMM's data
+ *   allows (its switching activity sets the clock the chip can hold).
  * Errors as for the GEMM: FP8BQ_ERR_SHAPE, _NULL, _ALIGN, _DEVICE, _LAUNCH.
  */
 int fp8bq_mb_read(const void *buf, int64_t bytes, int grid, unsigned *sink, void *stream);
 int fp8bq_mb_empty(int grid, int block, void *stream);
 int fp8bq_mb_mfma_e4m3(int grid, int iters, int code, float *sink, void *stream);
+int fp8bq_mb_mfma_e4m3_data(int grid, int iters, const void *codes, float *sink, void *stream);
 
 /* Human-readable name of a status code; never NULL. */
 const char *fp8bq_status_string(int status);

@@ -62,6 +62,7 @@ void dispatch_log(const char* entry, int64_t m, int64_t n, int64_t k, const char
 hipError_t launch_mb_read(const void* buf, int64_t bytes, int grid, unsigned* sink, hipStream_t stream);
 hipError_t launch_mb_empty(int grid, int block, hipStream_t stream);
 hipError_t launch_mb_mfma(int grid, int iters, unsigned code, float* sink, hipStream_t stream);
+hipError_t launch_mb_mfma_data(int grid, int iters, const void* codes, float* sink, hipStream_t stream);
 
 // C = 0 (used for K == 0).
 hipError_t launch_fill_zero_bf16(int64_t count, void* c, hipStream_t stream);

@@ -4,12 +4,13 @@
 // Page 1 (SmartX blog, "single-stream optimisation") reports a decode step
 // as bytes moved per step over time against a calibrated bandwidth, and its
 // "test background" section calibrates the tools before measuring. The same
-// is done here with three kernels:
+// is done here with four kernels:
 //  - a plain streaming read of a buffer (the most a weight-streaming GEMM of
 //    that many bytes could reach per call, launch and ramp included);
 //  - an empty kernel (the fixed cost of one launch in a stream);
 //  - a loop of independent FP8 16x16x128 MFMAs (the matrix-core rate the
-//    clock actually sustains).
+//    clock actually sustains), on one repeated code or on operands read from
+//    memory (realistic data: the rate the power budget allows a GEMM).
 #include "device_common.h"
 #include "launch.h"
 
@@ -82,6 +83,36 @@ __global__ __launch_bounds__(256) void mb_mfma_kernel(int iters, unsigned code, 
   sink[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
 }
 
+// The same loop with operands read from memory: chain u's first and second
+// operand in lane l are the 32 bytes at codes + 32 ((2 u + o) 64 + l),
+// o = 0, 1 (32 KB, shared by every wave). With realistic codes (quantised
+// Gaussian values rather than one repeated byte) the matrix core's switching
+// activity, and with it the clock the chip can hold, is that of a real GEMM.
+// Thread t writes the sum of its 32 accumulator values to sink[t].
+__global__ __launch_bounds__(256) void mb_mfma_data_kernel(int iters, const v4u* __restrict__ codes,
+                                                           float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  v8i a[8], b[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const v4u* pa = codes + 2 * ((2 * u) * 64 + lane);
+    const v4u* pb = codes + 2 * ((2 * u + 1) * 64 + lane);
+    a[u] = join8(pa[0], pa[1]);
+    b[u] = join8(pb[0], pb[1]);
+  }
+  v4f acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = mfma_16x16x128_e4m3_acc(a[u], b[u], acc[u]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) s += (acc[u][0] + acc[u][1]) + (acc[u][2] + acc[u][3]);
+  sink[static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x] = s;
+}
+
 }  // namespace
 
 hipError_t launch_mb_read(const void* buf, int64_t bytes, int grid, unsigned* sink, hipStream_t stream) {
@@ -96,6 +127,11 @@ hipError_t launch_mb_empty(int grid, int block, hipStream_t stream) {
 
 hipError_t launch_mb_mfma(int grid, int iters, unsigned code, float* sink, hipStream_t stream) {
   hipLaunchKernelGGL(mb_mfma_kernel, dim3(grid), dim3(256), 0, stream, iters, code, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_mb_mfma_data(int grid, int iters, const void* codes, float* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(mb_mfma_data_kernel, dim3(grid), dim3(256), 0, stream, iters, static_cast<const v4u*>(codes), sink);
   return hipGetLastError();
 }
 

@@ -35,6 +35,31 @@ def test_mfma_loop_closed_form(code, value):
     assert torch.all(sink == 4096.0 * iters * value * value)
 
 
+# Operands from memory: small codes (0, +-0.5, +-1, +-2) keep every sum
+# exact in fp32, so the GPU's per-thread sums must equal the closed form of
+# the documented operand layout: lane l's element i (row r = 4 (l / 16) + i,
+# column c = l % 16) sums dec(first[16 q + r][b]) * dec(second[16 q + c][b])
+# over q = 0..3 and byte b = 0..31.
+def test_mfma_data_loop_matches_its_operands():
+    from oracle import e4m3_decode
+
+    rng = np.random.default_rng(11)
+    codes = rng.choice(np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x40, 0xC0], dtype=np.uint8),
+                       size=fp8bq.MB_MFMA_DATA_BYTES)
+    iters, grid = 37, 5
+    sink = fp8bq.mb_mfma_data(grid, iters, torch.from_numpy(codes).cuda())
+    torch.cuda.synchronize()
+    dec = e4m3_decode(codes).reshape(8, 2, 64, 32)  # chain, operand, lane, byte
+    want = np.zeros(64)
+    for lane in range(64):
+        for i in range(4):
+            r, c = 4 * (lane // 16) + i, lane % 16
+            for u in range(8):
+                want[lane] += sum(float(np.dot(dec[u, 0, 16 * q + r], dec[u, 1, 16 * q + c])) for q in range(4))
+    got = sink.cpu().numpy().reshape(grid * 4, 64)
+    assert np.array_equal(got, np.broadcast_to((iters * want).astype(np.float32), got.shape))
+
+
 def test_empty_launch():
     for _ in range(10):
         fp8bq.mb_empty(256, 512)
