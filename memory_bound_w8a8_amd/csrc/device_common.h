@@ -119,8 +119,8 @@ __device__ __forceinline__ float quotient_e4m3_range(float x, float s, float y) 
 // multiply), once per group; per value q = fma(x, y_hi, x y_lo): 2 VALU
 // operations. For every bf16 x with |x| <= amax and every bf16 amax >= 2^-96
 // the e4m3 code of q equals that of the IEEE division x / s except that
-// x = -0 may give +0 (tests/quotient_check.c checks all 1.05e9 pairs on the
-// host). No clamp is needed: |q| <= 448 (1 + 2^-23), and the hardware
+// x = -0 may give +0 (tests/quotient_check.c checks the same 5.2e8 pairs on
+// the host). No clamp is needed: |q| <= 448 (1 + 2^-23), and the hardware
 // conversion rounds magnitudes up to 464 to 448 (it returns the NaN code only
 // above 464).
 struct RecipPair {
