@@ -101,7 +101,10 @@ int fp8bq_quant_weight(int64_t N, int64_t K, const float *W_f32, void *W_fp8, fl
  * nearest-size table): M <= 64 streams the weights once; M > 64 runs the
  * LDS-tiled MFMA kernel, whose tile shape (64x64 up to 256x256 tokens x
  * weight rows) follows from (M, N) by the number of rounds of workgroups
- * its grid needs on the 256 CUs. The summation order differs from the fp64
+ * its grid needs on the 256 CUs (for the 192x256 and 256x256 tiles a last
+ * round of at most 128 tiles runs as a second launch of column halves,
+ * with the same per-output summation order). The summation order differs
+ * from the fp64
  * definition; results agree within fp32 accumulation plus bf16 rounding.
  * Two identical calls give bitwise-identical C (no atomics).
  * K == 0 writes zeros. Errors: NULL pointer; negative size; K % 128 != 0;
