@@ -166,10 +166,11 @@ hipError_t tiled_instance(int64_t m, int64_t n, int64_t k, const void* aq, const
 // The 8-wave two-stage tiles (192 x 256, 256 x 256): gemm_tiled2_kernel,
 // unclamped when every row of every tile exists once the last token tile is
 // shifted back (M >= BM, N a multiple of BN, a tile's rows within 32-bit
-// copy offsets). A last round of at most 128 tiles after whole rounds (e.g. M = 3465 on
-// (5120, 8704): 380 tiles of 192 x 256 = 256 + 124) runs as a second launch
-// of column halves, 2 x 124 workgroups of 192 x 128 in one round at about
-// half a round's time, instead of 124 whole tiles leaving half the CUs idle.
+// copy offsets). A last round of at most 128 tiles after whole rounds
+// (e.g. M = 3465 on (5120, 8704): 380 tiles of 192 x 256 = 256 + 124) runs
+// as a second launch of column halves, 2 x 124 workgroups of 192 x 128 in
+// one round (measured at 0.66 of a whole round's time), instead of 124
+// whole tiles leaving half the CUs idle.
 template <int BM, int BN, bool CLAMP>
 void tiled2_launch(int64_t m, int64_t n, int64_t k, int64_t t0, int split, int64_t grid, const void* aq,
                    const float* as, const void* wq, const float* ws, void* c, hipStream_t stream) {
@@ -200,6 +201,8 @@ hipError_t tiled2_instance(int64_t m, int64_t n, int64_t k, const void* aq, cons
       tiled2_launch<BM, BN, false>(m, n, k, 0, 1, plan.whole, aq, as, wq, ws, c, stream);
     else
       tiled2_launch<BM, BN, true>(m, n, k, 0, 1, plan.whole, aq, as, wq, ws, c, stream);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   if (plan.halves > 0) {
     if (exact)
