@@ -5,7 +5,7 @@
 //   workgroup per CU; at most 16 * kMaxTiles rows, beyond that more
 //   workgroups), TILES = ceil(R / 16), and with S = 8 waves splitting the
 //   K / 128 groups, GMAX = ceil(groups / 8).
-// M only selects a token class (1..8, 9..16, 17..32, 33..64; see
+// M only selects a token class (1..8, 9..16, 17..32, 33..48, 49..64; see
 // rows_entry), so every M inside a class runs the same instruction stream. Each (TILES, GMAX)
 // pair has its own compiled instance, looked up exactly; shapes outside the
 // table (very large K) run the generic streaming kernel, which handles any
@@ -28,13 +28,13 @@ namespace fp8bq {
 
 namespace {
 
-template <int TILES, int GMAX>
+template <int TILES, int GMAX, int MSX = 4>
 hipError_t rows64_instance(const GemmArgs& a, int64_t rows_per_wg) {
   // with one row tile the activation fragments in flight dominate the
   // register budget: keep fewer weight chunks ahead
   constexpr int PD = TILES == 1 ? 2 : 3;
   const unsigned grid = static_cast<unsigned>((a.n + rows_per_wg - 1) / rows_per_wg);
-  hipLaunchKernelGGL((gemm_rows64_kernel<GMAX, TILES, PD>), dim3(grid), dim3(64 * kRowsWaves), 0, a.stream,
+  hipLaunchKernelGGL((gemm_rows64_kernel<GMAX, TILES, PD, MSX>), dim3(grid), dim3(64 * kRowsWaves), 0, a.stream,
                      static_cast<int>(a.m), a.n, a.k, rows_per_wg, static_cast<const unsigned char*>(a.aq), a.as,
                      static_cast<const unsigned char*>(a.wq), a.ws, static_cast<unsigned short*>(a.c));
   return hipGetLastError();
@@ -45,10 +45,14 @@ hipError_t rows64_instance(const GemmArgs& a, int64_t rows_per_wg) {
 // and transposed; the 32-token tile walks the chunks group-major when a
 // wave has more than 6 groups, so that only the groups in use are held --
 // with up to 2 row tiles; with more, those registers still do not fit and
-// the 64-token kernel serves), and 33..64 tokens (gemm_rows64.h).
+// the 64-token kernel serves), and 33..48 and 49..64 tokens
+// (gemm_rows64.h with three or four 16-token sub-tiles: at M = 33..48 the
+// three cost 3-10% less than four on the five logged shapes).
 template <int TT, int TILES, int GMAX>
 constexpr Launch rows_entry() {
-  if constexpr (TT == 64 || (TT == 32 && GMAX > 6 && TILES > 2))
+  if constexpr (TT == 48)
+    return &rows64_instance<TILES, GMAX, 3>;
+  else if constexpr (TT == 64 || (TT == 32 && GMAX > 6 && TILES > 2))
     return &rows64_instance<TILES, GMAX>;
   else if constexpr (TT == 8)
     return &rows_instance<16, kActCodes, TILES, GMAX>;
@@ -93,6 +97,7 @@ constexpr auto kW8A16 = w8a16_table(std::make_integer_sequence<int, kMaxTiles>{}
 constexpr auto kRows8 = rows_table<8>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows16 = rows_table<16>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows32 = rows_table<32>(std::make_integer_sequence<int, kMaxTiles>{});
+constexpr auto kRows48 = rows_table<48>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows64 = rows_table<64>(std::make_integer_sequence<int, kMaxTiles>{});
 
 template <int MT, int R, int S, int U>
@@ -122,7 +127,7 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
   int64_t rows_per_wg;
   int tiles, gmax;
   if (rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) {
-    const auto& table = m <= 8 ? kRows8 : m <= 16 ? kRows16 : m <= 32 ? kRows32 : kRows64;
+    const auto& table = m <= 8 ? kRows8 : m <= 16 ? kRows16 : m <= 32 ? kRows32 : m <= 48 ? kRows48 : kRows64;
     const char* kernel = m <= 8    ? "gemm_rows_kernel MT=16 act=codes"
                          : m <= 16 ? "gemm_rows_kernel MT=16 act=lines"
                          : m <= 32 ? (gmax > 6 && tiles > 2 ? "gemm_rows64_kernel" : "gemm_rows_kernel MT=32 act=lines")

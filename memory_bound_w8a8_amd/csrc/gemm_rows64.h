@@ -1,4 +1,5 @@
-// Weight-streaming split-K block-FP8 GEMM for 33..64 tokens, gfx950.
+// Weight-streaming split-K block-FP8 GEMM for 33..64 tokens, gfx950: 33..48
+// tokens as three 16-token sub-tiles (MSX = 3), 49..64 as four.
 //
 // Still HBM-bound (about 2 M flop per weight byte, far below the FP8 MFMA
 // ridge), so the design is the row-range streaming one of gemm_rows.h: one
@@ -19,19 +20,19 @@
 //
 // Reduction: after the last chunk every wave holds fp32 partials of all its
 // tiles. Two row tiles at a time, the 8 waves park them in LDS and wave w
-// sums (tile 2 r + w / 4, sub-tile w % 4) over the waves in order 0..7
-// (deterministic, no atomics), rounds to bf16 (RNE) and stores 4 consecutive
-// outputs per lane.
+// sums (tile 2 r + w / MS, sub-tile w % MS) over the waves in order 0..7
+// (deterministic, no atomics; with three sub-tiles waves 6 and 7 sit this
+// out), rounds to bf16 (RNE) and stores 4 consecutive outputs per lane.
 #pragma once
 
 #include "device_common.h"
 
 namespace fp8bq {
 
-template <int GMAX, int TILES, int PD>
+template <int GMAX, int TILES, int PD, int MSX = 4>
 struct Rows64Kernel {
   static constexpr int kWaves = 8;
-  static constexpr int kMS = 4;                                // 16-token sub-tiles
+  static constexpr int kMS = MSX;                              // 16-token sub-tiles (3 or 4)
   static constexpr int kChunks = TILES * GMAX;
   static constexpr int kRing = PD + 1;                         // weight chunk buffers
   static constexpr int kActSlots = (PD + TILES - 1) / TILES + 1;  // activation groups live at once
@@ -42,14 +43,15 @@ struct Rows64Kernel {
 // global stores in flight (__syncthreads() would also wait for those).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int GMAX, int TILES, int PD>
+template <int GMAX, int TILES, int PD, int MSX = 4>
 __global__ __launch_bounds__(512) void gemm_rows64_kernel(int m_rows, int64_t n, int64_t k, int64_t rows_per_wg,
                                                           const unsigned char* __restrict__ aq,
                                                           const float* __restrict__ as,
                                                           const unsigned char* __restrict__ wq,
                                                           const float* __restrict__ ws,
                                                           unsigned short* __restrict__ c) {
-  using KC = Rows64Kernel<GMAX, TILES, PD>;
+  using KC = Rows64Kernel<GMAX, TILES, PD, MSX>;
+  static_assert(MSX == 3 || MSX == 4, "48- or 64-token tiles");
   constexpr int S = KC::kWaves;
   constexpr int MS = KC::kMS;
   constexpr int CH = KC::kChunks;
@@ -98,13 +100,13 @@ __global__ __launch_bounds__(512) void gemm_rows64_kernel(int m_rows, int64_t n,
   // time; half-line requests spread over 16 token rows concentrate on a few
   // L2 channels and queue there.) The raw lines are transposed into the
   // MFMA operand when the group starts.
-  v4u araw[AS][8];
+  v4u araw[AS][2 * MS];
   float sa[AS][MS];
   auto load_act = [&](int u) {
     const bool live = u < gcnt;
     const uint32_t g = static_cast<uint32_t>(live ? gbeg + u : glast);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 2 * MS; ++j) {
       const uint32_t m = static_cast<uint32_t>(8 * j + (lane >> 3));
       araw[u % AS][j] = buffer_load16(ars, m * ku + static_cast<uint32_t>((lane & 7) * 16), g * kGroup);
     }
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(512) void gemm_rows64_kernel(int m_rows, int64_t n,
 #pragma unroll
         for (int s = 0; s < MS; ++s) red[wave][p][s][lane] = acc[t0 + p][s];
     lds_barrier();
-    if (t0 + rp < TILES) {
+    if (rp < PAIR && t0 + rp < TILES) {
       v4f sum = red[0][rp][rs][lane];
 #pragma unroll
       for (int w = 1; w < S; ++w) sum += red[w][rp][rs][lane];

@@ -67,7 +67,7 @@ TABLE_SHAPES = [(1000, 9216), (12800, 1024), (20000, 2304), (4100, 5120), (5000,
 
 
 @pytest.mark.parametrize("n,k", TABLE_SHAPES)
-@pytest.mark.parametrize("m", [1, 3, 8, 16, 17, 32, 33, 64])
+@pytest.mark.parametrize("m", [1, 3, 8, 16, 17, 32, 33, 48, 49, 64])
 def test_streaming_instance_table(m, n, k):
     a = workloads.activation(m, n, k)
     a_q, a_s = quant_act_ref(a)
@@ -94,7 +94,7 @@ def _integer_problem(m, n, k, vmax, scales, seed):
     return a_q, a_s, w_q, w_s
 
 
-@pytest.mark.parametrize("m", [1, 2, 5, 8, 16, 32, 64, 65, 200])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 16, 32, 40, 64, 65, 200])
 def test_integer_exact_bitwise_k1024(m):
     # |codes| <= 8, scales in {1/2, 1, 2}, K = 1024: every group sum, scaled
     # term and running sum is a multiple of 1/4 below 2^18, exact in fp32 in
@@ -222,7 +222,7 @@ def _full_cases():
         if (n, k) == (8192, 5120):
             ms = [1, 8, 16, 32, 64, 192]  # 128 x 64 tiles
         if (n, k) == (17408, 5120):
-            ms = list(range(1, 9)) + [16, 32, 64]
+            ms = list(range(1, 9)) + [16, 32, 40, 48, 64]
         if (n, k) == (5120, 8704):
             ms = [1, 8, 16, 17, 32, 64, 65, 128]
         if (n, k) == (7168, 5120):
