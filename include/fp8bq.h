@@ -98,7 +98,10 @@ int fp8bq_quant_weight(int64_t N, int64_t K, const float *W_f32, void *W_fp8, fl
  *   W_fp8    [N, K] uint8 codes,  W_scales [ceil(N/128), K/128] fp32 (read)
  *   C_bf16   [M, N] bf16, written, fp32 accumulation rounded to bf16 RNE.
  * Every M >= 1 is served by a kernel chosen from explicit ranges (no
- * nearest-size table): M <= 64 streams the weights once; M > 64 runs the
+ * nearest-size table): M <= 64 streams the weights once, and so does
+ * 65 <= M <= 80 where one round of 256 workgroups covers N with at most 32
+ * weight rows each and K <= 5120 (five 16-token sub-tiles; the registers
+ * of larger shapes spill); every other M > 64 runs the
  * LDS-tiled MFMA kernel, whose tile shape (64x64 up to 256x256 tokens x
  * weight rows) follows from (M, N) by the number of rounds of workgroups
  * its grid needs on the 256 CUs (for the 192x256 and 256x256 tiles a last
@@ -138,7 +141,7 @@ int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K);
 /*
  * The tile shape the LDS-tiled kernel takes for (M, N, K), as the
  * FP8BQ_PATH_TILED_* value fp8bq_gemm_forced accepts (fp8bq_gemm uses it
- * for M > 64; any M >= 1 is answered): the shape with the least grid
+ * where it does not stream; any M >= 1 is answered): the shape with the least grid
  * rounds on the 256 CUs times measured step cost. FP8BQ_PATH_NONE for
  * M == 0 or N == 0, a negative status for invalid sizes. Host-only: no
  * device is needed.
@@ -147,7 +150,8 @@ int fp8bq_gemm_tile_shape(int64_t M, int64_t N, int64_t K);
 
 /*
  * fp8bq_gemm with the kernel path forced (FP8BQ_PATH_STREAM requires
- * M <= 128, as two launches past 64 tokens; FP8BQ_PATH_TILED and the
+ * M <= 128, as one launch where fp8bq_gemm streams and otherwise two
+ * launches past 64 tokens; FP8BQ_PATH_TILED and the
  * FP8BQ_PATH_TILED_* shapes accept any M). For cross-checking the paths and
  * tile shapes at the same M: every tile shape sums each output in the same
  * order, so their results are bitwise equal. Same arguments, semantics and errors as fp8bq_gemm, plus

@@ -60,18 +60,22 @@ int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A_fp8, const fl
   return FP8BQ_OK;
 }
 
-// 1..64 tokens stream the weights once; beyond, the tiled kernel, whose
-// 4-wave 64 x 64 to 128 x 128 tiles keep the CUs filled at 65..128 tokens
-// (streaming the weights twice, tokens 0..63 and then the rest, measured
-// 15-30% slower on the N = 5120..8192 shapes and 15% on N = 17408).
-int gemm_path(int64_t M) {
-  if (M <= kStreamMaxM) return FP8BQ_PATH_STREAM;
+// 1..64 tokens stream the weights once, and 65..80 too where the five
+// sub-tile instances fit in registers (at most 2 row tiles per workgroup
+// and 5 groups per wave: N <= 8192 and K <= 5120; 7-12% faster there than
+// the tiled kernel). Beyond, the tiled kernel, whose 4-wave 64 x 64 to
+// 128 x 128 tiles keep the CUs filled at 65..128 tokens (streaming the
+// weights twice, tokens 0..63 and then the rest, measured 15-30% slower on
+// the N = 5120..8192 shapes and 15% on N = 17408).
+int gemm_path(int64_t M, int64_t N, int64_t K) {
+  if (M <= kStreamMaxM || fp8bq::stream_wide_serves(M, N, K)) return FP8BQ_PATH_STREAM;
   return FP8BQ_PATH_TILED;
 }
 
 hipError_t launch_stream_split(int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales,
                                const void* W_fp8, const float* W_scales, void* C_bf16, hipStream_t s) {
-  if (M <= kStreamMaxM) return fp8bq::launch_gemm_stream(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s);
+  if (M <= kStreamMaxM || fp8bq::stream_wide_serves(M, N, K))
+    return fp8bq::launch_gemm_stream(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s);
   const hipError_t e = fp8bq::launch_gemm_stream(kStreamMaxM, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s);
   if (e != hipSuccess) return e;
   return fp8bq::launch_gemm_stream(M - kStreamMaxM, N, K, static_cast<const unsigned char*>(A_fp8) + kStreamMaxM * K,
@@ -126,7 +130,7 @@ int fp8bq_quant_weight(int64_t N, int64_t K, const float* W_f32, void* W_fp8, fl
 int fp8bq_gemm(int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales, const void* W_fp8,
                const float* W_scales, void* C_bf16, void* stream) {
   if (M < 0 || N < 0) return FP8BQ_ERR_SHAPE;
-  return run_gemm(gemm_path(M), M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
+  return run_gemm(gemm_path(M, N, K), M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
 }
 
 int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales,
@@ -138,7 +142,7 @@ int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
   if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_PATH_NONE;
-  return gemm_path(M);
+  return gemm_path(M, N, K);
 }
 
 int fp8bq_gemm_tile_shape(int64_t M, int64_t N, int64_t K) {

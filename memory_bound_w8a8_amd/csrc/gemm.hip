@@ -1,12 +1,15 @@
 // Kernel instances and launch configuration of the block-FP8 GEMM.
 //
-// Streaming path (M <= 64). The launch shape follows from (N, K) alone:
+// Streaming path (M <= 64, and 65..80 where the registers allow: at most 2
+// row tiles per workgroup and 5 groups per wave). The launch shape follows
+// from (N, K) alone:
 //   rows per workgroup R = N / 256 rounded up to a multiple of 4 (one
 //   workgroup per CU; at most 16 * kMaxTiles rows, beyond that more
 //   workgroups), TILES = ceil(R / 16), and with S = 8 waves splitting the
 //   K / 128 groups, GMAX = ceil(groups / 8).
-// M only selects a token class (1..8, 9..16, 17..32, 33..48, 49..64; see
-// rows_entry), so every M inside a class runs the same instruction stream. Each (TILES, GMAX)
+// M only selects a token class (1..8, 9..16, 17..32, 33..48, 49..64, 65..80;
+// see rows_entry), so every M inside a class runs the same instruction
+// stream. Each (TILES, GMAX)
 // pair has its own compiled instance, looked up exactly; shapes outside the
 // table (very large K) run the generic streaming kernel, which handles any
 // size with runtime loops.
@@ -28,6 +31,11 @@ namespace fp8bq {
 
 namespace {
 
+// 65..80 tokens stream only where a workgroup holds at most this many row
+// tiles and a wave at most this many groups (both limits by register use)
+constexpr int kWideMaxTiles = 2;
+constexpr int kWideMaxGroups = 5;
+
 template <int TILES, int GMAX, int MSX = 4>
 hipError_t rows64_instance(const GemmArgs& a, int64_t rows_per_wg) {
   // with one row tile the activation fragments in flight dominate the
@@ -45,12 +53,21 @@ hipError_t rows64_instance(const GemmArgs& a, int64_t rows_per_wg) {
 // and transposed; the 32-token tile walks the chunks group-major when a
 // wave has more than 6 groups, so that only the groups in use are held --
 // with up to 2 row tiles; with more, those registers still do not fit and
-// the 64-token kernel serves), and 33..48 and 49..64 tokens
-// (gemm_rows64.h with three or four 16-token sub-tiles: at M = 33..48 the
-// three cost 3-10% less than four on the five logged shapes).
+// the 64-token kernel serves), and 33..48, 49..64 and 65..80 tokens
+// (gemm_rows64.h with three, four or five 16-token sub-tiles: at M = 33..48
+// the three cost 3-10% less than four on the five logged shapes; five at
+// 65..80 cost 7-12% less than the tiled kernel where they fit).
 template <int TT, int TILES, int GMAX>
 constexpr Launch rows_entry() {
-  if constexpr (TT == 48)
+  if constexpr (TT == 80) {
+    // 65..80 tokens, five sub-tiles: only where a workgroup has at most 2
+    // row tiles and a wave at most 5 groups (beyond, the accumulators and
+    // the held activation no longer fit in registers and spill)
+    if constexpr (TILES <= kWideMaxTiles && GMAX <= kWideMaxGroups)
+      return &rows64_instance<TILES, GMAX, 5>;
+    else
+      return nullptr;
+  } else if constexpr (TT == 48)
     return &rows64_instance<TILES, GMAX, 3>;
   else if constexpr (TT == 64 || (TT == 32 && GMAX > 6 && TILES > 2))
     return &rows64_instance<TILES, GMAX>;
@@ -98,6 +115,7 @@ constexpr auto kRows8 = rows_table<8>(std::make_integer_sequence<int, kMaxTiles>
 constexpr auto kRows16 = rows_table<16>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows32 = rows_table<32>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows48 = rows_table<48>(std::make_integer_sequence<int, kMaxTiles>{});
+constexpr auto kRows80 = rows_table<80>(std::make_integer_sequence<int, kMaxTiles>{});
 constexpr auto kRows64 = rows_table<64>(std::make_integer_sequence<int, kMaxTiles>{});
 
 template <int MT, int R, int S, int U>
@@ -126,6 +144,13 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
   const GemmArgs a{m, n, k, aq, as, wq, ws, c, stream};
   int64_t rows_per_wg;
   int tiles, gmax;
+  if (m > 64) {  // 65..80 tokens, only where stream_wide_serves
+    if (!stream_wide_serves(m, n, k)) return hipErrorInvalidValue;
+    rows_shape(n, k, &rows_per_wg, &tiles, &gmax);
+    dispatch_log("gemm(stream)", m, n, k,
+                 rows_desc("gemm_rows64_kernel MS=5", n, rows_per_wg, tiles, gmax).c_str());
+    return kRows80[tiles - 1][gmax - 1](a, rows_per_wg);
+  }
   if (rows_shape(n, k, &rows_per_wg, &tiles, &gmax)) {
     const auto& table = m <= 8 ? kRows8 : m <= 16 ? kRows16 : m <= 32 ? kRows32 : m <= 48 ? kRows48 : kRows64;
     const char* kernel = m <= 8    ? "gemm_rows_kernel MT=16 act=codes"
@@ -140,6 +165,13 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
   if (m <= 16) return stream_instance<16, 1, 8, 5>(a);
   if (m <= 32) return stream_instance<32, 1, 8, 4>(a);
   return stream_instance<64, 1, 8, 2>(a);
+}
+
+bool stream_wide_serves(int64_t m, int64_t n, int64_t k) {
+  int64_t rows_per_wg;
+  int tiles, gmax;
+  return m > 64 && m <= 80 && rows_shape(n, k, &rows_per_wg, &tiles, &gmax) && tiles <= kWideMaxTiles &&
+         gmax <= kWideMaxGroups;
 }
 
 bool small_m_supported(int64_t m, int64_t n, int64_t k) {

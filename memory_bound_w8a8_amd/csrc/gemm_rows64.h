@@ -1,5 +1,7 @@
-// Weight-streaming split-K block-FP8 GEMM for 33..64 tokens, gfx950: 33..48
-// tokens as three 16-token sub-tiles (MSX = 3), 49..64 as four.
+// Weight-streaming split-K block-FP8 GEMM for 33..80 tokens, gfx950: 33..48
+// tokens as three 16-token sub-tiles (MSX = 3), 49..64 as four, 65..80 as
+// five (only with at most 2 row tiles and 5 groups per wave, where the
+// accumulators and activation fragments still fit in registers).
 //
 // Still HBM-bound (about 2 M flop per weight byte, far below the FP8 MFMA
 // ridge), so the design is the row-range streaming one of gemm_rows.h: one
@@ -19,10 +21,12 @@
 // load counter never makes a wait cover loads issued later than needed.
 //
 // Reduction: after the last chunk every wave holds fp32 partials of all its
-// tiles. Two row tiles at a time, the 8 waves park them in LDS and wave w
-// sums (tile 2 r + w / MS, sub-tile w % MS) over the waves in order 0..7
-// (deterministic, no atomics; with three sub-tiles waves 6 and 7 sit this
-// out), rounds to bf16 (RNE) and stores 4 consecutive outputs per lane.
+// tiles. Two row tiles at a time, the 8 waves park them in LDS; the 2 * MS
+// (tile, sub-tile) items of the round go to the waves in turn (item i to
+// wave i mod 8: with three sub-tiles waves 6 and 7 sit out, with five waves
+// 0 and 1 take a second item), and each sums its item over the waves in
+// order 0..7 (deterministic, no atomics), rounds to bf16 (RNE) and stores 4
+// consecutive outputs per lane.
 #pragma once
 
 #include "device_common.h"
@@ -32,7 +36,7 @@ namespace fp8bq {
 template <int GMAX, int TILES, int PD, int MSX = 4>
 struct Rows64Kernel {
   static constexpr int kWaves = 8;
-  static constexpr int kMS = MSX;                              // 16-token sub-tiles (3 or 4)
+  static constexpr int kMS = MSX;                              // 16-token sub-tiles (3, 4 or 5)
   static constexpr int kChunks = TILES * GMAX;
   static constexpr int kRing = PD + 1;                         // weight chunk buffers
   static constexpr int kActSlots = (PD + TILES - 1) / TILES + 1;  // activation groups live at once
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(512) void gemm_rows64_kernel(int m_rows, int64_t n,
                                                           const float* __restrict__ ws,
                                                           unsigned short* __restrict__ c) {
   using KC = Rows64Kernel<GMAX, TILES, PD, MSX>;
-  static_assert(MSX == 3 || MSX == 4, "48- or 64-token tiles");
+  static_assert(MSX >= 3 && MSX <= 5, "48-, 64- or 80-token tiles");
   constexpr int S = KC::kWaves;
   constexpr int MS = KC::kMS;
   constexpr int CH = KC::kChunks;
@@ -193,8 +197,6 @@ __global__ __launch_bounds__(512) void gemm_rows64_kernel(int m_rows, int64_t n,
     }
   }
 
-  const int rp = wave / MS;  // tile of the pair this wave reduces
-  const int rs = wave % MS;  // its 16-token sub-tile
 #pragma unroll
   for (int t0 = 0; t0 < TILES; t0 += PAIR) {
 #pragma unroll
@@ -203,7 +205,14 @@ __global__ __launch_bounds__(512) void gemm_rows64_kernel(int m_rows, int64_t n,
 #pragma unroll
         for (int s = 0; s < MS; ++s) red[wave][p][s][lane] = acc[t0 + p][s];
     lds_barrier();
-    if (rp < PAIR && t0 + rp < TILES) {
+    // items (tile of the pair, sub-tile) = (it / MS, it % MS), it = wave,
+    // wave + 8, ...
+#pragma unroll
+    for (int it0 = 0; it0 < PAIR * MS; it0 += S) {
+      const int it = it0 + wave;
+      const int rp = it / MS;
+      const int rs = it % MS;
+      if (it >= PAIR * MS || t0 + rp >= TILES) continue;
       v4f sum = red[0][rp][rs][lane];
 #pragma unroll
       for (int w = 1; w < S; ++w) sum += red[w][rp][rs][lane];

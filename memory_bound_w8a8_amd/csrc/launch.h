@@ -23,6 +23,9 @@ hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, co
 // The small-M entry points below serve 1 <= m <= 16 and K/128 groups within
 // the streaming instance table.
 bool small_m_supported(int64_t m, int64_t n, int64_t k);
+// Whether 65..96 tokens on (N, K) have a streaming instance (at most two
+// 16-row tiles per workgroup).
+bool stream_wide_serves(int64_t m, int64_t n, int64_t k);
 
 // Activation quantisation fused into the streaming GEMM (bf16 activation in).
 hipError_t launch_gemm_fused(int64_t m, int64_t n, int64_t k, const void* a, const void* wq, const float* ws, void* c,

@@ -225,10 +225,17 @@ def test_gemm_path_dispatch_by_explicit_m_ranges(fp8bq):
         assert L.fp8bq_gemm_path(m, 17408, 5120) == fp8bq.PATH_STREAM, m
     for m in (65, 128, 2048, 3465, 4096):
         assert L.fp8bq_gemm_path(m, 17408, 5120) == fp8bq.PATH_TILED, m
-    # beyond 64 tokens the tiled kernel on every weight shape
-    for n in (128, 5120, 7168, 8192, 16256):
-        for m in (65, 100, 128, 129):
-            assert L.fp8bq_gemm_path(m, n, 5120) == fp8bq.PATH_TILED, (m, n)
+    # 65..80 tokens stream where one round of 256 workgroups covers N with
+    # at most 32 rows each (N <= 8192) and a wave holds at most 5 of the
+    # K/128 groups (K <= 5120); otherwise, and beyond 80, the tiled kernel
+    for n, k in ((5120, 3072), (7168, 5120), (8192, 5120), (128, 1024), (8192, 128)):
+        for m in (65, 72, 80):
+            assert L.fp8bq_gemm_path(m, n, k) == fp8bq.PATH_STREAM, (m, n, k)
+        for m in (81, 100, 128, 129, 3465):
+            assert L.fp8bq_gemm_path(m, n, k) == fp8bq.PATH_TILED, (m, n, k)
+    for n, k in ((5120, 8704), (17408, 5120), (8193, 5120), (8192, 5248), (16256, 5120)):
+        for m in (65, 80, 81, 128):
+            assert L.fp8bq_gemm_path(m, n, k) == fp8bq.PATH_TILED, (m, n, k)
     assert L.fp8bq_gemm_path(1, 17408, 5000) == -2
 
 

@@ -23,6 +23,11 @@ for m in (1, 3, 1, 16, 32, 64, 65, 3465):
     a_q, a_s = fp8bq.quant_act(torch.randn(m, k, device=dev).to(torch.bfloat16))
     fp8bq.gemm(a_q, a_s, w_q, w_s)
 fp8bq.gemm_fused(torch.randn(2, k, device=dev).to(torch.bfloat16), w_q, w_s)
+# 65..80 tokens stream where a workgroup has 2 row tiles and a wave 5 groups
+w_q, w_s = fp8bq.quant_weight(torch.randn(8192, k, device=dev) * 0.02)
+for m in (80, 81):
+    a_q, a_s = fp8bq.quant_act(torch.randn(m, k, device=dev).to(torch.bfloat16))
+    fp8bq.gemm(a_q, a_s, w_q, w_s)
 # tile shapes by rounds x step cost on (5120, 8704): 192 x 256 at the prefill size,
 # 128 x 256 where it keeps the grid within the same rounds
 w_q, w_s = fp8bq.quant_weight(torch.randn(5120, 8704, device=dev) * 0.02)
@@ -48,6 +53,9 @@ def test_dispatch_log_names_each_decision_once():
     assert got["fp8bq: gemm(stream) M=64 N=17408 K=5120"].startswith("gemm_rows64_kernel")
     assert got["fp8bq: gemm(tiled) M=65 N=17408 K=5120"].startswith("gemm_tiled_kernel BM=128 BN=128")
     assert got["fp8bq: gemm(tiled) M=3465 N=17408 K=5120"].startswith("gemm_tiled2_kernel BM=256 BN=256 8 waves 2 stages grid=952")
+    assert got["fp8bq: gemm(stream) M=80 N=8192 K=5120"] == (
+        "gemm_rows64_kernel MS=5 TILES=2 GMAX=5 rows/wg=32 grid=256")
+    assert got["fp8bq: gemm(tiled) M=81 N=8192 K=5120"].startswith("gemm_tiled")
     assert got["fp8bq: gemm_fused M=2 N=17408 K=5120"].startswith("gemm_rows_kernel MT=16 act=bf16 TOK=2")
     # 380 tiles of 192 x 256 (one round, then the last 124 tiles as 248 column halves in about half a
     # round) beat 280 of 256 x 256 (one round + 48 halves) and 560 of 128 x 256 (2.19 rounds)

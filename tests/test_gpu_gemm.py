@@ -83,6 +83,35 @@ def test_streaming_instance_table(m, n, k):
         assert_gemm_close(c[rows, cols], ref, what=f"M={m} N={n} K={k} (sampled)")
 
 
+# 65..80 tokens stream with five 16-token sub-tiles where a workgroup has at
+# most 2 row tiles and a wave at most 5 groups: every (tiles, groups) pair
+# of that table, ragged N (not a multiple of 4, a short last tile), and the
+# class's first, middle and last M.
+WIDE_SHAPES = [(4000, 128), (3000, 2048), (4096, 3072), (1000, 4096), (2500, 5120),
+               (5001, 384), (6000, 2560), (7000, 4096), (8190, 5120), (4100, 1152)]
+
+
+@pytest.mark.parametrize("n,k", WIDE_SHAPES)
+@pytest.mark.parametrize("m", [65, 72, 80])
+def test_streaming_wide_token_class(m, n, k):
+    assert fp8bq.lib().fp8bq_gemm_path(m, n, k) == fp8bq.PATH_STREAM
+    a = workloads.activation(m, n, k)
+    a_q, a_s = quant_act_ref(a)
+    w_q, w_s = quant_weight_ref(workloads.weight(n, k))
+    c = _gpu_gemm(a_q, a_s, w_q, w_s)
+    if n * k <= 12_000_000:
+        assert_gemm_close(c, gemm_ref(a_q, a_s, w_q, w_s), what=f"M={m} N={n} K={k}")
+    else:
+        rng = np.random.default_rng([m, n, k])
+        rows = rng.integers(0, m, 3000)
+        cols = np.concatenate([rng.integers(0, n, 2000), np.arange(n - 1000, n)])
+        ref = gemm_ref_at(a_q, a_s, w_q, w_s, rows, cols)
+        assert_gemm_close(c[rows, cols], ref, what=f"M={m} N={n} K={k} (sampled)")
+    # the forced streaming path is the same single launch here
+    c_forced = _gpu_gemm(a_q, a_s, w_q, w_s, path=fp8bq.PATH_STREAM)
+    assert np.array_equal(c, c_forced)
+
+
 def _integer_problem(m, n, k, vmax, scales, seed):
     rng = np.random.default_rng(seed)
     vals = np.arange(-vmax, vmax + 1, dtype=np.float32)
@@ -94,7 +123,7 @@ def _integer_problem(m, n, k, vmax, scales, seed):
     return a_q, a_s, w_q, w_s
 
 
-@pytest.mark.parametrize("m", [1, 2, 5, 8, 16, 32, 40, 64, 65, 200])
+@pytest.mark.parametrize("m", [1, 2, 5, 8, 16, 32, 40, 64, 65, 80, 81, 200])
 def test_integer_exact_bitwise_k1024(m):
     # |codes| <= 8, scales in {1/2, 1, 2}, K = 1024: every group sum, scaled
     # term and running sum is a multiple of 1/4 below 2^18, exact in fp32 in
@@ -117,7 +146,7 @@ def test_integer_exact_bitwise_k8704(m):
         assert np.array_equal(c, want), f"M={m} N={n}"
 
 
-@pytest.mark.parametrize("m", [1, 3, 8, 64, 130])
+@pytest.mark.parametrize("m", [1, 3, 8, 64, 72, 130])
 def test_integer_exact_bitwise_k5120(m):
     # |codes| <= 2, scales in {1, 2}, K = 5120 (40 groups split over waves):
     # group sums < 2^10, running sums < 2^17, all integers: exact in fp32.
@@ -218,15 +247,15 @@ def _full_cases():
         if (n, k) == (5120, 3072):
             # both token classes of the 2-tile, 3-groups-per-wave instances
             # (9..16 and 17..32), and 64 x 128 tiles at 256
-            ms = [1, 8, 9, 12, 16, 17, 24, 32, 64, 256]
+            ms = [1, 8, 9, 12, 16, 17, 24, 32, 64, 65, 80, 256]
         if (n, k) == (8192, 5120):
-            ms = [1, 8, 16, 32, 64, 192]  # 128 x 64 tiles
+            ms = [1, 8, 16, 32, 64, 80, 192]  # 128 x 64 tiles at 192
         if (n, k) == (17408, 5120):
             ms = list(range(1, 9)) + [16, 32, 40, 48, 64]
         if (n, k) == (5120, 8704):
             ms = [1, 8, 16, 17, 32, 64, 65, 128]
         if (n, k) == (7168, 5120):
-            ms = [1, 8, 16, 32, 64, 100]
+            ms = [1, 8, 16, 32, 64, 65, 100]
         if (n, k) in workloads.PREFILL_SHAPES:
             ms.append(workloads.PREFILL_M)
         cases += [(m, n, k) for m in ms]
