@@ -104,6 +104,18 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Wave priority (0..3) for the instruction arbiter of a SIMD. The two
+// waves sharing a SIMD otherwise take the matrix core in age order: the
+// older one runs its whole K step first and the younger one finishes alone.
+__device__ __forceinline__ void set_prio(int level) {
+  switch (level) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
 // Tile index of workgroup b: XCD-contiguous runs of the tile space.
 __device__ __forceinline__ int64_t xcd_tile(int64_t b, int64_t tiles) {
   const int64_t x = b & 7, s = b >> 3;
@@ -382,6 +394,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
 //    reads, then those MFMAs (operands already in registers), which cover
 //    the latency of the new reads; each weight fragment is refilled right
 //    after the MFMA that last uses it.
+//  - The two waves that share a SIMD would otherwise take the matrix core in
+//    age order (a per-wave timestamp trace showed the older wave finishing
+//    its K step about 1,000 cycles before the younger one, which then ran
+//    alone); the wave's priority steps down from 3 to 0 over the step's
+//    sub-tiles, so whichever wave is behind in the step is preferred, and
+//    the barrier resets it (M = 3465: 2-3% less time on (17408, 5120) and
+//    (5120, 8704); issuing the copies two sub-tiles after the barrier
+//    instead helped the first and cost the second 5%).
 //  - CLAMP = false (every row of the tile exists: M >= BM, N a multiple of
 //    BN): the last token tile is shifted back to end at row M - 1 and stores
 //    only the rows the previous tile does not, so no row is clamped and one
@@ -584,6 +604,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
     for (int j = 0; j < J - 1; ++j) {
       const v8i af_n = a_frag(st, j + 1);
       const float sa_n = a_scale(st, j + 1);
+      set_prio(3 - (3 * (j + 1)) / (J - 1));
       mfma_row((j + J - 1) % J, sa * sw, nothing);
       af = af_n;
       sa = sa_n;
@@ -596,6 +617,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
       // have landed (own copies: vmcnt; everyone's: the barrier)
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      set_prio(3);
       const int64_t g2 = g + 2 < groups ? g + 2 : groups - 1;
       issue(g2, st);
       const v8i af_n = a_frag(SN{}, 0);
