@@ -186,6 +186,20 @@ def time_kernels(plan, reps):
 FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA
 
 
+def scaled_mfma_tflops(dev, grid=1024, iters=4096):
+    """FP8 16x16x128 MFMA rate of the block-scaled GEMM's inner loop (fresh
+    products, 4 fp32 scale FMAs per MFMA) on quantised Gaussian codes: the
+    most a GEMM that scales each group's products gets from the matrix
+    cores on this GPU."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    vals = torch.randn(fp8bq.MB_MFMA_DATA_BYTES, generator=g, device=dev).mul_(448.0 / 4.0)
+    codes = vals.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    us = graph_us(lambda i: fp8bq.mb_mfma_scaled(grid, iters, codes, 0.5, sink=sink), 3)
+    return grid * 4 * 8 * iters * 2.0 * 16 * 16 * 128 / us / 1e6
+
+
 def prefill(plan, reps=20):
     """Prefill GEMMs (M = 3465 tokens, page 2 section 4.2) on the two logged
     shapes that take it, timed with HIP events on the launch stream around
@@ -195,6 +209,7 @@ def prefill(plan, reps=20):
     dev = plan.dev
     m = workloads.PREFILL_M
     out = []
+    scaled_loop = scaled_mfma_tflops(dev)
     g = torch.Generator(device=dev)
     for n, k in workloads.PREFILL_SHAPES:
         if (n, k) == (N, K):
@@ -234,6 +249,8 @@ def prefill(plan, reps=20):
         tflops = 2.0 * m * n * k / (us * 1e-6) / 1e12
         out.append({"M": m, "N": n, "K": k, "us": round(us, 2), "us_windows": [round(w, 2) for w in windows],
                     "TFLOPs": round(tflops, 1), "frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4),
+                    "scaled_mfma_loop_TFLOPs": round(scaled_loop, 1),
+                    "frac_of_scaled_mfma_loop": round(tflops / scaled_loop, 4),
                     "vendor_fp8_gemm_context": vendor_fp8_gemm(m, n, k, reps)})
         del a, aq, as_, c
     return out
@@ -497,7 +514,9 @@ def ceilings():
     - one empty launch of the decode kernels' grid (256 x 512): the fixed
       cost each call pays;
     - the FP8 16x16x128 MFMA rate of 1024 workgroups x 4 waves x 8
-      independent chains (the matrix-core peak at the clock this load runs)."""
+      independent chains (the matrix-core peak at the clock this load runs),
+      on one code, on quantised Gaussian codes, and with the block-scaled
+      GEMM's 4 fp32 scale FMAs per MFMA."""
     dev = torch.device("cuda:0")
     sizes = [(f"({n}, {k}) at M=1", gemm_bytes(1, n, k)) for n, k in workloads.SHAPES]
     sizes += [("vocabulary projection (152064, 5120)", 152064 * 5120), ("1 GiB", 1 << 30)]
@@ -528,14 +547,20 @@ def ceilings():
     vals = torch.randn(fp8bq.MB_MFMA_DATA_BYTES, generator=g, device=dev).mul_(448.0 / 4.0)
     codes = vals.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
     data_us = graph_us(lambda i: fp8bq.mb_mfma_data(grid, iters, codes, sink=msink), 3)
+    # and in the block-scaled GEMM's inner loop (fresh products, 4 fp32
+    # scale FMAs per MFMA): the most a per-group-scaled GEMM gets from the
+    # matrix cores
+    scaled = scaled_mfma_tflops(dev, grid, iters)
     print(f"bench: MFMA loop {flops / mfma_us / 1e6:.0f} TFLOP/s (one code), {flops / data_us / 1e6:.0f} "
-          "(Gaussian codes)", file=sys.stderr, flush=True)
+          f"(Gaussian codes), {scaled:.0f} (Gaussian codes, 4 scale FMAs per MFMA)", file=sys.stderr, flush=True)
     return {"read": read, "empty_launch_us": round(empty_us, 3),
             "mfma_e4m3_16x16x128": {"TFLOPs": round(flops / mfma_us / 1e6, 1), "us": round(mfma_us, 1),
                                     "frac_of_5000": round(flops / mfma_us / 1e6 / FP8_PEAK_TFLOPS, 4)},
             "mfma_e4m3_16x16x128_gaussian_codes": {
                 "TFLOPs": round(flops / data_us / 1e6, 1), "us": round(data_us, 1),
-                "frac_of_5000": round(flops / data_us / 1e6 / FP8_PEAK_TFLOPS, 4)}}
+                "frac_of_5000": round(flops / data_us / 1e6 / FP8_PEAK_TFLOPS, 4)},
+            "mfma_e4m3_16x16x128_gaussian_codes_scale_fmas": {
+                "TFLOPs": round(scaled, 1), "frac_of_5000": round(scaled / FP8_PEAK_TFLOPS, 4)}}
 
 
 PER_SHAPE_M = [1, 2, 3, 4, 5, 6, 7, 8, 16, 32, 64]

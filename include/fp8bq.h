@@ -299,7 +299,7 @@ int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void *h
  * roofline fractions against besides the published peaks (page 1, SmartX
  * blog: "single-stream optimisation" reports bytes per decode step over time
  * against a calibrated bandwidth; "test background" calibrates the tools
- * first). All four only read their inputs and write `sink`.
+ * first). All five only read their inputs and write `sink`.
  *
  * fp8bq_mb_read: streaming read of `bytes` bytes at `buf` (bytes % 16 == 0,
  *   buf 16-B aligned) by `grid` (1..65536) workgroups of 512 threads,
@@ -327,12 +327,23 @@ int fp8bq_rescore_bf16(int64_t M, int64_t K, int64_t V, int64_t k, const void *h
  *   elements (8 chains x 4) to sink[t] (sink [grid * 256] fp32). With
  *   quantised Gaussian codes this is the matrix-core rate a GEMM's data
  *   allows (its switching activity sets the clock the chip can hold).
+ * fp8bq_mb_mfma_e4m3_scaled: the block-scaled GEMM's inner loop on the same
+ *   operands (page 2, ownding.com L20 report, section 8: the W8A8 block FP8
+ *   GEMM, one scale per 128-wide group): every MFMA starts from zero and its
+ *   4 results per lane are folded into the chain's running sums by 4 fp32
+ *   FMAs with `scale`, one MFMA later, so that the matrix core and the VALU
+ *   share each SIMD as in fp8bq_gemm's tiled kernel. sink: `scale` times
+ *   the sums of fp8bq_mb_mfma_e4m3_data (exact when both are). The rate
+ *   this loop reaches is the most a GEMM that scales every group's products
+ *   in fp32 can get from the matrix cores.
  * Errors as for the GEMM: FP8BQ_ERR_SHAPE, _NULL, _ALIGN, _DEVICE, _LAUNCH.
  */
 int fp8bq_mb_read(const void *buf, int64_t bytes, int grid, unsigned *sink, void *stream);
 int fp8bq_mb_empty(int grid, int block, void *stream);
 int fp8bq_mb_mfma_e4m3(int grid, int iters, int code, float *sink, void *stream);
 int fp8bq_mb_mfma_e4m3_data(int grid, int iters, const void *codes, float *sink, void *stream);
+int fp8bq_mb_mfma_e4m3_scaled(int grid, int iters, const void *codes, float scale, float *sink,
+                              void *stream);
 
 /* Human-readable name of a status code; never NULL. */
 const char *fp8bq_status_string(int status);

@@ -52,6 +52,7 @@ EXPORTS = (
     "fp8bq_mb_empty",
     "fp8bq_mb_mfma_e4m3",
     "fp8bq_mb_mfma_e4m3_data",
+    "fp8bq_mb_mfma_e4m3_scaled",
     "fp8bq_status_string",
 )
 
@@ -93,13 +94,15 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_mb_empty.argtypes = [ci, ci, vp]
         L.fp8bq_mb_mfma_e4m3.argtypes = [ci, ci, ci, vp, vp]
         L.fp8bq_mb_mfma_e4m3_data.argtypes = [ci, ci, vp, vp, vp]
+        L.fp8bq_mb_mfma_e4m3_scaled.argtypes = [ci, ci, vp, ctypes.c_float, vp, vp]
         L.fp8bq_status_string.argtypes = [ctypes.c_int]
         L.fp8bq_status_string.restype = ctypes.c_char_p
         for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path",
                      "fp8bq_gemm_tile_shape",
                      "fp8bq_gemm_w8a16", "fp8bq_gemm_fused", "fp8bq_topk_bf16", "fp8bq_topk_bf16_noalloc",
                      "fp8bq_rescore_bf16",
-                     "fp8bq_mb_read", "fp8bq_mb_empty", "fp8bq_mb_mfma_e4m3", "fp8bq_mb_mfma_e4m3_data"):
+                     "fp8bq_mb_read", "fp8bq_mb_empty", "fp8bq_mb_mfma_e4m3", "fp8bq_mb_mfma_e4m3_data",
+                     "fp8bq_mb_mfma_e4m3_scaled"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -388,4 +391,19 @@ def mb_mfma_data(grid: int, iters: int, codes: torch.Tensor, sink: torch.Tensor 
     _check("fp8bq_mb_mfma_e4m3_data",
            lib().fp8bq_mb_mfma_e4m3_data(int(grid), int(iters), _ptr(codes), _ptr(sink),
                                          torch.cuda.current_stream(codes.device).cuda_stream))
+    return sink
+
+
+def mb_mfma_scaled(grid: int, iters: int, codes: torch.Tensor, scale: float, sink: torch.Tensor = None) -> torch.Tensor:
+    """mb_mfma_data's operands in the block-scaled GEMM's inner loop: every
+    MFMA from zero, its results folded into running sums by 4 fp32 FMAs with
+    `scale`; returns the per-thread sums (fp32 [grid * 256], `scale` times
+    mb_mfma_data's)."""
+    if codes.dtype != torch.uint8 or codes.numel() != MB_MFMA_DATA_BYTES or not codes.is_contiguous():
+        raise ValueError("codes: contiguous uint8 tensor of 32768 bytes")
+    if sink is None:
+        sink = torch.empty(grid * 256, dtype=torch.float32, device=codes.device)
+    _check("fp8bq_mb_mfma_e4m3_scaled",
+           lib().fp8bq_mb_mfma_e4m3_scaled(int(grid), int(iters), _ptr(codes), float(scale), _ptr(sink),
+                                           torch.cuda.current_stream(codes.device).cuda_stream))
     return sink

@@ -293,4 +293,14 @@ int fp8bq_mb_mfma_e4m3_data(int grid, int iters, const void* codes, float* sink,
   return launch_status(fp8bq::launch_mb_mfma_data(grid, iters, codes, sink, static_cast<hipStream_t>(stream)));
 }
 
+int fp8bq_mb_mfma_e4m3_scaled(int grid, int iters, const void* codes, float scale, float* sink, void* stream) {
+  if (grid < 1 || grid > 65536 || iters < 0 || iters > (1 << 24)) return FP8BQ_ERR_SHAPE;
+  if (codes == nullptr || sink == nullptr) return FP8BQ_ERR_NULL;
+  if (!aligned(codes, 16) || !aligned(sink, 4)) return FP8BQ_ERR_ALIGN;
+  const int st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(
+      fp8bq::launch_mb_mfma_scaled(grid, iters, codes, scale, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

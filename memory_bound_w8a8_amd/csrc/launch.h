@@ -66,6 +66,8 @@ hipError_t launch_mb_read(const void* buf, int64_t bytes, int grid, unsigned* si
 hipError_t launch_mb_empty(int grid, int block, hipStream_t stream);
 hipError_t launch_mb_mfma(int grid, int iters, unsigned code, float* sink, hipStream_t stream);
 hipError_t launch_mb_mfma_data(int grid, int iters, const void* codes, float* sink, hipStream_t stream);
+hipError_t launch_mb_mfma_scaled(int grid, int iters, const void* codes, float scale, float* sink,
+                                 hipStream_t stream);
 
 // C = 0 (used for K == 0).
 hipError_t launch_fill_zero_bf16(int64_t count, void* c, hipStream_t stream);

@@ -10,7 +10,8 @@
 //  - an empty kernel (the fixed cost of one launch in a stream);
 //  - a loop of independent FP8 16x16x128 MFMAs (the matrix-core rate the
 //    clock actually sustains), on one repeated code or on operands read from
-//    memory (realistic data: the rate the power budget allows a GEMM).
+//    memory (realistic data: the rate the power budget allows a GEMM), and
+//    the same with the block-scaled GEMM's 4 scale FMAs per MFMA.
 #include "device_common.h"
 #include "launch.h"
 
@@ -89,7 +90,14 @@ __global__ __launch_bounds__(256) void mb_mfma_kernel(int iters, unsigned code, 
 // Gaussian values rather than one repeated byte) the matrix core's switching
 // activity, and with it the clock the chip can hold, is that of a real GEMM.
 // Thread t writes the sum of its 32 accumulator values to sink[t].
-__global__ __launch_bounds__(256) void mb_mfma_data_kernel(int iters, const v4u* __restrict__ codes,
+//
+// SCALED: the block-scaled GEMM's inner loop instead. Every MFMA starts from
+// zero (one 128-wide scale group per instruction) and its result is folded
+// into the chain's running sum by 4 fp32 FMAs with `scale`, one MFMA later
+// (acc += scale * previous product), so the matrix core and the VALU work
+// side by side as in the GEMM: thread t writes scale times the same sum.
+template <bool SCALED>
+__global__ __launch_bounds__(256) void mb_mfma_data_kernel(int iters, const v4u* __restrict__ codes, float scale,
                                                            float* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
   v8i a[8], b[8];
@@ -103,9 +111,29 @@ __global__ __launch_bounds__(256) void mb_mfma_data_kernel(int iters, const v4u*
   v4f acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int it = 0; it < iters; ++it) {
+  if constexpr (SCALED) {
+    v4f prev[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = mfma_16x16x128_e4m3_acc(a[u], b[u], acc[u]);
+    for (int u = 0; u < 8; ++u) prev[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const v4f p = mfma_16x16x128_e4m3(a[u], b[u]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[u][e] = fmaf(scale, prev[u][e], acc[u][e]);
+        asm volatile("" : "+v"(acc[u]));
+        prev[u] = p;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[u][e] = fmaf(scale, prev[u][e], acc[u][e]);
+  } else {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = mfma_16x16x128_e4m3_acc(a[u], b[u], acc[u]);
+    }
   }
   float s = 0.f;
 #pragma unroll
@@ -131,7 +159,15 @@ hipError_t launch_mb_mfma(int grid, int iters, unsigned code, float* sink, hipSt
 }
 
 hipError_t launch_mb_mfma_data(int grid, int iters, const void* codes, float* sink, hipStream_t stream) {
-  hipLaunchKernelGGL(mb_mfma_data_kernel, dim3(grid), dim3(256), 0, stream, iters, static_cast<const v4u*>(codes), sink);
+  hipLaunchKernelGGL(mb_mfma_data_kernel<false>, dim3(grid), dim3(256), 0, stream, iters,
+                     static_cast<const v4u*>(codes), 1.f, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_mb_mfma_scaled(int grid, int iters, const void* codes, float scale, float* sink,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(mb_mfma_data_kernel<true>, dim3(grid), dim3(256), 0, stream, iters,
+                     static_cast<const v4u*>(codes), scale, sink);
   return hipGetLastError();
 }
 

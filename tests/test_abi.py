@@ -33,7 +33,8 @@ def test_header_declares_the_abi():
                            "fp8bq_gemm_forced", "fp8bq_gemm_tile_shape", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16",
                            "fp8bq_topk_workspace_bytes",
                            "fp8bq_topk_bf16", "fp8bq_topk_bf16_noalloc", "fp8bq_rescore_bf16", "fp8bq_mb_read", "fp8bq_mb_empty",
-                           "fp8bq_mb_mfma_e4m3", "fp8bq_mb_mfma_e4m3_data", "fp8bq_status_string"}
+                           "fp8bq_mb_mfma_e4m3", "fp8bq_mb_mfma_e4m3_data", "fp8bq_mb_mfma_e4m3_scaled",
+                           "fp8bq_status_string"}
 
 
 def test_library_exports_every_declared_symbol(fp8bq):
@@ -288,6 +289,14 @@ def test_measurement_kernel_argument_errors(fp8bq):
     assert L.fp8bq_mb_mfma_e4m3_data(1, 1, p, None, None) == -1
     assert L.fp8bq_mb_mfma_e4m3_data(1, 1, p + 8, p, None) == -3
     assert L.fp8bq_mb_mfma_e4m3_data(1, 1, p, p + 2, None) == -3
+    assert L.fp8bq_mb_mfma_e4m3_scaled(0, 1, p, 1.0, p, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3_scaled(65537, 1, p, 1.0, p, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3_scaled(1, -1, p, 1.0, p, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3_scaled(1, 1 << 25, p, 1.0, p, None) == -2
+    assert L.fp8bq_mb_mfma_e4m3_scaled(1, 1, None, 1.0, p, None) == -1
+    assert L.fp8bq_mb_mfma_e4m3_scaled(1, 1, p, 1.0, None, None) == -1
+    assert L.fp8bq_mb_mfma_e4m3_scaled(1, 1, p + 8, 1.0, p, None) == -3
+    assert L.fp8bq_mb_mfma_e4m3_scaled(1, 1, p, 1.0, p + 2, None) == -3
 
 
 def test_tile_shape_rule_takes_the_measured_choices(fp8bq):

@@ -60,6 +60,33 @@ def test_mfma_data_loop_matches_its_operands():
     assert np.array_equal(got, np.broadcast_to((iters * want).astype(np.float32), got.shape))
 
 
+def test_mfma_scaled_loop_is_scale_times_the_plain_loop():
+    # the block-scaled inner loop (fresh products, 4 scale FMAs each, one
+    # MFMA later) against the closed form: scale times the plain loop's sums;
+    # codes in {0, +-0.5, +-1, +-2} and scale 0.75 keep every value exact
+    from oracle import e4m3_decode
+
+    rng = np.random.default_rng(12)
+    codes = rng.choice(np.array([0x00, 0x30, 0xB0, 0x38, 0xB8, 0x40, 0xC0], dtype=np.uint8),
+                       size=fp8bq.MB_MFMA_DATA_BYTES)
+    iters, grid, scale = 29, 3, 0.75
+    sink = fp8bq.mb_mfma_scaled(grid, iters, torch.from_numpy(codes).cuda(), scale)
+    torch.cuda.synchronize()
+    dec = e4m3_decode(codes).reshape(8, 2, 64, 32)  # chain, operand, lane, byte
+    want = np.zeros(64)
+    for lane in range(64):
+        for i in range(4):
+            r, c = 4 * (lane // 16) + i, lane % 16
+            for u in range(8):
+                want[lane] += sum(float(np.dot(dec[u, 0, 16 * q + r], dec[u, 1, 16 * q + c])) for q in range(4))
+    got = sink.cpu().numpy().reshape(grid * 4, 64)
+    assert np.array_equal(got, np.broadcast_to((scale * iters * want).astype(np.float32), got.shape))
+    # zero iterations: nothing accumulated
+    sink = fp8bq.mb_mfma_scaled(grid, 0, torch.from_numpy(codes).cuda(), scale)
+    torch.cuda.synchronize()
+    assert torch.all(sink == 0)
+
+
 def test_empty_launch():
     for _ in range(10):
         fp8bq.mb_empty(256, 512)
