@@ -39,6 +39,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "wave_prio.h"
 
 namespace fp8bq {
 
@@ -102,18 +103,6 @@ template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-// Wave priority (0..3) for the instruction arbiter of a SIMD. The two
-// waves sharing a SIMD otherwise take the matrix core in age order: the
-// older one runs its whole K step first and the younger one finishes alone.
-__device__ __forceinline__ void set_prio(int level) {
-  switch (level) {
-    case 0: __builtin_amdgcn_s_setprio(0); break;
-    case 1: __builtin_amdgcn_s_setprio(1); break;
-    case 2: __builtin_amdgcn_s_setprio(2); break;
-    default: __builtin_amdgcn_s_setprio(3); break;
-  }
 }
 
 // Tile index of workgroup b: XCD-contiguous runs of the tile space.
