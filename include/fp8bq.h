@@ -162,6 +162,47 @@ int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_f
                       void *C_bf16, void *stream);
 
 /*
+ * fp8bq_gemm with a caller-provided device workspace: the same operation,
+ * arguments, semantics and errors, plus the workspace. Where fp8bq_gemm
+ * runs the LDS-tiled kernel (beyond 64 tokens) and its tiles would leave
+ * CUs idle (M = 65..~256 on the logged shapes: 20..136 tiles for 256 CUs),
+ * the workspace lets the K/128 groups of each tile be split over several
+ * workgroups: each part writes an fp32 partial tile into the workspace and
+ * a second launch adds the parts in a fixed order and rounds to bf16 (RNE).
+ * Identical calls give identical bits; the split changes the summation
+ * order, so results can differ from fp8bq_gemm's in the last bits (both
+ * agree with the fp64 definition within fp32 accumulation plus bf16
+ * rounding).
+ *   workspace        device memory, 16-B aligned, workspace_bytes long (NULL
+ *                    only with workspace_bytes == 0); overwritten. Calls
+ *                    sharing a workspace must be ordered (same stream).
+ *   workspace_bytes  >= fp8bq_gemm_workspace_bytes(M, N, K) > 0: the split
+ *                    plan runs; otherwise exactly fp8bq_gemm's kernels run
+ *                    (bitwise equal to fp8bq_gemm).
+ * Errors: as fp8bq_gemm, plus FP8BQ_ERR_SHAPE for workspace_bytes < 0,
+ * FP8BQ_ERR_NULL for a NULL workspace with workspace_bytes > 0 and
+ * FP8BQ_ERR_ALIGN for a workspace not 16-B aligned.
+ *
+ * fp8bq_gemm_workspace_bytes: the bytes the split plan for (M, N, K) takes
+ * (split x M x N x 4), 0 where fp8bq_gemm_ws does not split, or a negative
+ * status for invalid sizes. Host-only: no device is needed.
+ *
+ * fp8bq_gemm_ws_forced: the split plan with the tile shape (an
+ * FP8BQ_PATH_TILED_* value: 128x128, 128x256, 64x128, 128x64 or 64x64)
+ * and the number of K parts (2 .. min(64, K/128)) forced, workspace_bytes
+ * >= split x M x N x 4; split == 1 runs fp8bq_gemm_forced(path, ...). For
+ * cross-checking plans: FP8BQ_ERR_SHAPE for a shape or split it cannot
+ * run.
+ */
+int64_t fp8bq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int fp8bq_gemm_ws(int64_t M, int64_t N, int64_t K, const void *A_fp8, const float *A_scales,
+                  const void *W_fp8, const float *W_scales, void *C_bf16, void *workspace,
+                  int64_t workspace_bytes, void *stream);
+int fp8bq_gemm_ws_forced(int path, int split, int64_t M, int64_t N, int64_t K, const void *A_fp8,
+                         const float *A_scales, const void *W_fp8, const float *W_scales,
+                         void *C_bf16, void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * Activation quantisation and block-FP8 GEMM in one launch (page 1, SmartX
  * blog, "single-stream optimisation": the W8A8 backend's per-call
  * activation quantisation is a separate launch at every linear layer; here

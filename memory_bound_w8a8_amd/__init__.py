@@ -41,6 +41,9 @@ EXPORTS = (
     "fp8bq_gemm",
     "fp8bq_gemm_path",
     "fp8bq_gemm_forced",
+    "fp8bq_gemm_workspace_bytes",
+    "fp8bq_gemm_ws",
+    "fp8bq_gemm_ws_forced",
     "fp8bq_gemm_tile_shape",
     "fp8bq_gemm_fused",
     "fp8bq_gemm_w8a16",
@@ -80,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_quant_weight.argtypes = [i64, i64, fp, vp, fp, vp]
         L.fp8bq_gemm.argtypes = [i64, i64, i64, vp, fp, vp, fp, vp, vp]
         L.fp8bq_gemm_forced.argtypes = [ctypes.c_int, i64, i64, i64, vp, fp, vp, fp, vp, vp]
+        L.fp8bq_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+        L.fp8bq_gemm_workspace_bytes.restype = i64
+        L.fp8bq_gemm_ws.argtypes = [i64, i64, i64, vp, fp, vp, fp, vp, vp, i64, vp]
+        L.fp8bq_gemm_ws_forced.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, fp, vp, fp, vp, vp, i64, vp]
         L.fp8bq_gemm_path.argtypes = [i64, i64, i64]
         L.fp8bq_gemm_tile_shape.argtypes = [i64, i64, i64]
         L.fp8bq_gemm_w8a16.argtypes = [i64, i64, i64, vp, vp, fp, vp, vp]
@@ -98,6 +105,7 @@ def lib() -> ctypes.CDLL:
         L.fp8bq_status_string.argtypes = [ctypes.c_int]
         L.fp8bq_status_string.restype = ctypes.c_char_p
         for name in ("fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_forced", "fp8bq_gemm_path",
+                     "fp8bq_gemm_ws", "fp8bq_gemm_ws_forced",
                      "fp8bq_gemm_tile_shape",
                      "fp8bq_gemm_w8a16", "fp8bq_gemm_fused", "fp8bq_topk_bf16", "fp8bq_topk_bf16_noalloc",
                      "fp8bq_rescore_bf16",
@@ -240,6 +248,48 @@ def gemm_forced(path: int, a_q, a_s, w_q, w_s, out=None) -> torch.Tensor:
         st = lib().fp8bq_gemm_forced(int(path), m, n, k, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(out),
                                      _stream(a_q))
     _check("fp8bq_gemm_forced", st)
+    return out
+
+
+def gemm_workspace_bytes(m: int, n: int, k: int) -> int:
+    """Device workspace bytes gemm_ws() uses for its K-split plan on (M, N, K)
+    (0: no split); raises on invalid sizes."""
+    st = lib().fp8bq_gemm_workspace_bytes(int(m), int(n), int(k))
+    if st < 0:
+        raise Fp8bqError("fp8bq_gemm_workspace_bytes", st)
+    return st
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace: contiguous uint8 tensor")
+    return workspace
+
+
+def gemm_ws(a_q, a_s, w_q, w_s, out=None, workspace=None) -> torch.Tensor:
+    """gemm() with a device workspace (uint8 tensor; allocated here when
+    None), which lets 65..~256-token calls split each tile's K range over
+    several workgroups (fp8bq_gemm_ws)."""
+    a_q, w_q, m, n, k, out = _gemm_args(a_q, a_s, w_q, w_s, out)
+    workspace = _workspace(gemm_workspace_bytes(m, n, k), a_q.device, workspace)
+    with torch.cuda.device(a_q.device):
+        st = lib().fp8bq_gemm_ws(m, n, k, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s), _ptr(out), _ptr(workspace),
+                                 workspace.numel(), _stream(a_q))
+    _check("fp8bq_gemm_ws", st)
+    return out
+
+
+def gemm_ws_forced(path: int, split: int, a_q, a_s, w_q, w_s, out=None, workspace=None) -> torch.Tensor:
+    """gemm_ws() with the tile shape (a PATH_TILED_* value) and the number of
+    K parts forced (split == 1: gemm_forced)."""
+    a_q, w_q, m, n, k, out = _gemm_args(a_q, a_s, w_q, w_s, out)
+    workspace = _workspace(int(split) * m * n * 4 if split > 1 else 0, a_q.device, workspace)
+    with torch.cuda.device(a_q.device):
+        st = lib().fp8bq_gemm_ws_forced(int(path), int(split), m, n, k, _ptr(a_q), _ptr(a_s), _ptr(w_q), _ptr(w_s),
+                                        _ptr(out), _ptr(workspace), workspace.numel(), _stream(a_q))
+    _check("fp8bq_gemm_ws_forced", st)
     return out
 
 

@@ -102,6 +102,21 @@ int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const
   return launch_status(fp8bq::launch_gemm_tiled(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, s, shape));
 }
 
+// Workspace bytes the K-split plan of fp8bq_gemm_ws needs for a valid
+// (M, N, K) with M, N, K > 0 (0 when the plan does not split).
+int64_t split_workspace_bytes(int64_t M, int64_t N, int64_t K, fp8bq::SplitPlan* plan) {
+  if (gemm_path(M, N, K) != FP8BQ_PATH_TILED || K >= kTiledMaxK) return 0;
+  *plan = fp8bq::split_plan(M, N, K);
+  return plan->split > 1 ? plan->split * M * N * 4 : 0;
+}
+
+int check_workspace(const void* workspace, int64_t workspace_bytes) {
+  if (workspace_bytes < 0) return FP8BQ_ERR_SHAPE;
+  if (workspace_bytes > 0 && workspace == nullptr) return FP8BQ_ERR_NULL;
+  if (workspace != nullptr && !aligned(workspace, 16)) return FP8BQ_ERR_ALIGN;
+  return FP8BQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,6 +153,60 @@ int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void* A_f
   return run_gemm(path, M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
 }
 
+int64_t fp8bq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
+  if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
+  if (M == 0 || N == 0 || K == 0) return 0;
+  fp8bq::SplitPlan plan;
+  return split_workspace_bytes(M, N, K, &plan);
+}
+
+int fp8bq_gemm_ws(int64_t M, int64_t N, int64_t K, const void* A_fp8, const float* A_scales, const void* W_fp8,
+                  const float* W_scales, void* C_bf16, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0) return FP8BQ_ERR_SHAPE;
+  int st = check_gemm_args(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16);
+  if (st != FP8BQ_OK) return st;
+  st = check_workspace(workspace, workspace_bytes);
+  if (st != FP8BQ_OK) return st;
+  if (M > 0 && N > 0 && K > 0) {
+    fp8bq::SplitPlan plan;
+    const int64_t need = split_workspace_bytes(M, N, K, &plan);
+    if (need > 0 && workspace_bytes >= need) {
+      st = check_device();
+      if (st != FP8BQ_OK) return st;
+      return launch_status(fp8bq::launch_gemm_split(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16,
+                                                    static_cast<float*>(workspace), plan.shape, plan.split,
+                                                    static_cast<hipStream_t>(stream)));
+    }
+  }
+  return run_gemm(gemm_path(M, N, K), M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
+}
+
+int fp8bq_gemm_ws_forced(int path, int split, int64_t M, int64_t N, int64_t K, const void* A_fp8,
+                         const float* A_scales, const void* W_fp8, const float* W_scales, void* C_bf16,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  if (split == 1) {
+    const int st = check_workspace(workspace, workspace_bytes);
+    if (st != FP8BQ_OK) return st;
+    return run_gemm(path, M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16, stream);
+  }
+  if (M < 0 || N < 0) return FP8BQ_ERR_SHAPE;
+  int st = check_gemm_args(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16);
+  if (st != FP8BQ_OK) return st;
+  st = check_workspace(workspace, workspace_bytes);
+  if (st != FP8BQ_OK) return st;
+  const int shape = path - FP8BQ_PATH_TILED_128x128;
+  const bool splits = shape == 0 || shape == 1 || shape == 4 || shape == 5 || shape == 6;
+  if (!splits || split < 2 || split > 64 || split > K / 128 || K >= kTiledMaxK) return FP8BQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return FP8BQ_OK;
+  if (workspace_bytes < split * M * N * 4) return FP8BQ_ERR_SHAPE;
+  st = check_device();
+  if (st != FP8BQ_OK) return st;
+  return launch_status(fp8bq::launch_gemm_split(M, N, K, A_fp8, A_scales, W_fp8, W_scales, C_bf16,
+                                                static_cast<float*>(workspace), shape, split,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int fp8bq_gemm_path(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
   if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
@@ -149,7 +218,7 @@ int fp8bq_gemm_tile_shape(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return FP8BQ_ERR_SHAPE;
   if (!product_ok(M, K) || !product_ok(N, K) || !product_ok(M, N)) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_PATH_NONE;
-  return FP8BQ_PATH_TILED_128x128 + fp8bq::tiled_shape(M, N);
+  return FP8BQ_PATH_TILED_128x128 + fp8bq::tiled_shape(M, N, nullptr);
 }
 
 int fp8bq_gemm_fused(int64_t M, int64_t N, int64_t K, const void* A_bf16, const void* W_fp8, const float* W_scales,

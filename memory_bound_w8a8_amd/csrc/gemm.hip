@@ -126,6 +126,34 @@ hipError_t stream_instance(const GemmArgs& a) {
   return hipGetLastError();
 }
 
+// C = bf16_rne(part[0] + part[1] + ... + part[split - 1]) elementwise, the
+// parts added in that order (deterministic): the K-split tiled path's second
+// launch. count = M * N; four outputs per thread when count % 4 == 0 (part
+// and c 16-byte aligned).
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int split, int64_t count,
+                                                           unsigned short* __restrict__ c) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if ((count & 3) == 0) {
+    const v4f* p = reinterpret_cast<const v4f*>(part);
+    const int64_t q4 = count >> 2;
+    for (int64_t q = first; q < q4; q += stride) {
+      v4f sum = p[q];
+      for (int s = 1; s < split; ++s) sum += p[s * q4 + q];
+      v2u packed;
+      packed[0] = pack_bf16x2(sum[0], sum[1]);
+      packed[1] = pack_bf16x2(sum[2], sum[3]);
+      reinterpret_cast<v2u*>(c)[q] = packed;
+    }
+  } else {
+    for (int64_t i = first; i < count; i += stride) {
+      float sum = part[i];
+      for (int s = 1; s < split; ++s) sum += part[s * count + i];
+      c[i] = static_cast<unsigned short>(pack_bf16x2(sum, 0.f) & 0xffffu);
+    }
+  }
+}
+
 __global__ void fill_zero_kernel(unsigned short* __restrict__ c, int64_t count) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) c[i] = 0;
@@ -190,13 +218,15 @@ hipError_t launch_gemm_w8a16(int64_t m, int64_t n, int64_t k, const void* a, con
   return kW8A16[tiles - 1][gmax - 1](args, rows_per_wg);
 }
 
+// One launch of gemm_tiled_kernel: the whole K range per tile into C, or
+// (split > 1) `split` K parts per tile into the fp32 partial tiles `part`.
 template <int BM, int BN, int WM, int WN, int STAGES>
 hipError_t tiled_instance(int64_t m, int64_t n, int64_t k, const void* aq, const float* as, const void* wq,
-                          const float* ws, void* c, hipStream_t stream) {
+                          const float* ws, void* c, hipStream_t stream, int split = 1, float* part = nullptr) {
   const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WM, WN, STAGES>), dim3(static_cast<unsigned>(tiles)), dim3(64 * WM * WN), 0,
-                     stream, m, n, k, static_cast<const unsigned char*>(aq), as,
-                     static_cast<const unsigned char*>(wq), ws, static_cast<unsigned short*>(c));
+  hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WM, WN, STAGES>), dim3(static_cast<unsigned>(tiles * split)),
+                     dim3(64 * WM * WN), 0, stream, m, n, k, split, static_cast<const unsigned char*>(aq), as,
+                     static_cast<const unsigned char*>(wq), ws, static_cast<unsigned short*>(c), part);
   return hipGetLastError();
 }
 
@@ -304,7 +334,7 @@ int64_t tile_count(int64_t m, int64_t n, const TileShape& t) { return ((m + t.bm
 // Equal costs go to the grid with more tiles (the better-filled machine),
 // then to the earlier shape in the order 64x64, 64x128, 128x64, 128x128,
 // 128x256, 192x256, 256x256.
-int tiled_shape(int64_t m, int64_t n) {
+int tiled_shape(int64_t m, int64_t n, int64_t* step_cost) {
   constexpr int kOrder[kNumTileShapes] = {6, 4, 5, 0, 1, 2, 3};
   int best = 0;
   int64_t best_cost = INT64_MAX, best_tiles = 0;
@@ -324,12 +354,94 @@ int tiled_shape(int64_t m, int64_t n) {
       best_tiles = tiles;
     }
   }
+  if (step_cost != nullptr) *step_cost = best_cost;
   return best;
+}
+
+// K-split plan for the tiled path when the caller gives a workspace
+// (fp8bq_gemm_ws). With few tiles (M = 65..~256 tokens: 20..136 tiles on
+// the logged shapes) most CUs sit idle while each tile walks all K/128
+// groups; splitting every tile's groups into `split` parts fills the CUs,
+// each part writing an fp32 partial tile, and a second launch adds the
+// parts in a fixed order. Costs in 1/100 us, fitted to measured times
+// (MI355X, the five logged shapes at M = 81, 128, 256, every splittable
+// shape x 2..24 parts; least squares, mean error 7%):
+//   split:   0.965 x rounds(tiles x split) x ceil(groups / split) x step
+//            cost + 0.418 us per MB of partial tiles (written once, read
+//            once) + 7.9 us (the second launch, the pipeline's fill and
+//            drain at short K ranges);
+//   unsplit: 1.146 x rounds(tiles) x groups x step cost - 1.8 us.
+// The split runs where its cost is the lower: e.g. M = 81 on (5120, 8704)
+// 128 x 128 tiles in 6 parts, 19.6 us against 29.5; on (17408, 5120)
+// 128 x 256 tiles in 3 parts, 31.7 against 37.3; not on (5120, 3072),
+// whose 24 groups leave too little K per part. Only the gemm_tiled_kernel
+// shapes split (not the two-stage 192 x 256 / 256 x 256 tiles).
+constexpr int64_t kSplitStepPerMille = 965;
+constexpr int64_t kSplitPerByteE7 = 418;  // 1/100 us per 10^7 bytes of partial tiles
+constexpr int64_t kSplitFixed = 790;
+constexpr int64_t kUnsplitPerMille = 1146;
+constexpr int64_t kUnsplitOffset = -178;
+constexpr int kMaxSplit = 64;
+
+SplitPlan split_plan(int64_t m, int64_t n, int64_t k) {
+  SplitPlan plan;
+  const int64_t groups = k / kGroup;
+  if (m < 1 || n < 1 || groups < 2) return plan;
+  int64_t step;
+  plan.shape = tiled_shape(m, n, &step);
+  plan.cost = kUnsplitPerMille * step * groups / 1000 + kUnsplitOffset;
+  constexpr int kSplitShapes[] = {6, 4, 5, 0, 1};
+  for (int i : kSplitShapes) {
+    const TileShape& t = kTileShapes[i];
+    const int64_t tiles = tile_count(m, n, t);
+    const int64_t cap = static_cast<int64_t>(kNumCUs) * t.per_cu;
+    for (int64_t sp = 2; sp <= groups && sp <= kMaxSplit; ++sp) {
+      const int64_t items = tiles * sp;
+      if (items > 4 * cap) break;
+      const int64_t rounds = (items + cap - 1) / cap;
+      const int64_t steps = (groups + sp - 1) / sp;
+      const int64_t compute = rounds * steps * (items > kNumCUs ? t.step_cost2 : t.step_cost);
+      const int64_t cost = kSplitStepPerMille * compute / 1000 + kSplitPerByteE7 * (sp * m * n * 4) / 10000000 +
+                           kSplitFixed;
+      if (cost < plan.cost) {
+        plan.shape = i;
+        plan.split = static_cast<int>(sp);
+        plan.cost = cost;
+      }
+    }
+  }
+  return plan;
+}
+
+hipError_t launch_gemm_split(int64_t m, int64_t n, int64_t k, const void* aq, const float* as, const void* wq,
+                             const float* ws, void* c, float* part, int shape, int split, hipStream_t stream) {
+  if (split < 2 || split > k / kGroup || (shape != 0 && shape != 1 && shape != 4 && shape != 5 && shape != 6))
+    return hipErrorInvalidValue;
+  const std::string desc = std::string(kTileShapes[shape].desc) + " grid=" +
+                           std::to_string(tile_count(m, n, kTileShapes[shape]) * split) + " (K in " +
+                           std::to_string(split) + " parts) + split_reduce_kernel";
+  dispatch_log("gemm(tiled, split K)", m, n, k, desc.c_str());
+  hipError_t e;
+  switch (shape) {
+    case 0: e = tiled_instance<128, 128, 2, 2, 3>(m, n, k, aq, as, wq, ws, c, stream, split, part); break;
+    case 1: e = tiled_instance<128, 256, 2, 4, 3>(m, n, k, aq, as, wq, ws, c, stream, split, part); break;
+    case 4: e = tiled_instance<64, 128, 1, 4, 3>(m, n, k, aq, as, wq, ws, c, stream, split, part); break;
+    case 5: e = tiled_instance<128, 64, 2, 2, 3>(m, n, k, aq, as, wq, ws, c, stream, split, part); break;
+    default: e = tiled_instance<64, 64, 2, 2, 3>(m, n, k, aq, as, wq, ws, c, stream, split, part); break;
+  }
+  if (e != hipSuccess) return e;
+  const int64_t count = m * n;
+  const int64_t per = (count & 3) == 0 ? count / 4 : count;
+  int64_t blocks = (per + 255) / 256;
+  blocks = blocks < 2048 ? blocks : 2048;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, part, split,
+                     count, static_cast<unsigned short*>(c));
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                              const void* wq, const float* ws, void* c, hipStream_t stream, int shape) {
-  if (shape < 0) shape = tiled_shape(m, n);
+  if (shape < 0) shape = tiled_shape(m, n, nullptr);
   if (shape >= kNumTileShapes) return hipErrorInvalidValue;
   std::string desc = std::string(kTileShapes[shape].desc) + " grid=" + std::to_string(tile_count(m, n, kTileShapes[shape]));
   if (shape == 2 || shape == 3) {

@@ -135,12 +135,13 @@ __device__ __forceinline__ void band_tile(int64_t t, int64_t m_tiles, int64_t n_
 }
 
 template <int BM, int BN, int WM, int WN, int STAGES>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows, int64_t n, int64_t k,
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows, int64_t n, int64_t k, int split,
                                                                   const unsigned char* __restrict__ aq,
                                                                   const float* __restrict__ as,
                                                                   const unsigned char* __restrict__ wq,
                                                                   const float* __restrict__ ws,
-                                                                  unsigned short* __restrict__ c) {
+                                                                  unsigned short* __restrict__ c,
+                                                                  float* __restrict__ part) {
   using KC = TiledKernel<BM, BN, WM, WN, STAGES>;
   constexpr int WAVES = KC::kWaves;
   constexpr int TM = KC::kTM, TN = KC::kTN, J = KC::kJ, I = KC::kI;
@@ -166,12 +167,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   const int quarter = lane >> 4;
   const int wave_m = wave % WM;
   const int wave_n = wave / WM;
-  const int64_t groups = k >> 7;
+  const int64_t gstride = k >> 7;  // scale groups per row of the scale arrays
 
+  // Workgroup -> (tile, K part): with split > 1 the grid is tiles x split
+  // workgroups, part s of a tile summing groups [G s / split, G (s + 1) /
+  // split) into an fp32 partial tile of `part` (split x M x N); the parts
+  // of one K range run next to each other, so an XCD's run of workgroups
+  // shares A and W slices as in the unsplit grid.
   const int64_t m_tiles = (m_rows + BM - 1) / BM;
   const int64_t n_tiles = (n + BN - 1) / BN;
+  const int64_t n_units = m_tiles * n_tiles;
+  const int64_t unit = xcd_tile(blockIdx.x, n_units * split);
+  const int64_t tile = unit % n_units;
+  const int64_t ks = unit / n_units;
+  const int64_t g_lo = gstride * ks / split;
+  const int64_t groups = gstride * (ks + 1) / split - g_lo;  // this workgroup's K steps (>= 1)
   int64_t tm, tn;
-  band_tile(xcd_tile(blockIdx.x, m_tiles * n_tiles), m_tiles, n_tiles, 8, &tm, &tn);
+  band_tile(tile, m_tiles, n_tiles, 8, &tm, &tn);
   const int64_t m0 = tm * BM;
   const int64_t n0 = tn * BN;
 
@@ -181,8 +193,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   const int cr = lane >> 3;                 // row within the 8-row chunk
   // Per-lane 32-bit offsets from the tile's first row (which sits in scalar
   // registers); a tile spans at most 256 rows of K bytes.
-  const unsigned char* a_base = aq + m0 * k;
-  const unsigned char* w_base = wq + n0 * k;
+  const unsigned char* a_base = aq + m0 * k + g_lo * kGroup;
+  const unsigned char* w_base = wq + n0 * k + g_lo * kGroup;
   unsigned a_off[A_CHUNKS];
   unsigned w_off[W_CHUNKS];
 #pragma unroll
@@ -201,13 +213,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   // 64 w .. 64 w + 63 (one dword each: a 64-line gather, so only as many
   // waves as there are distinct slots issue one).
   const bool copies_scales = wave < BM / 64;
-  const float* sa_base = as + m0 * groups;
+  const float* sa_base = as + m0 * gstride + g_lo;
   const int sa_t = 64 * (copies_scales ? wave : 0) + lane;
   const int64_t sa_r = m0 + sa_t < m_rows ? sa_t : m_rows - 1 - m0;
-  const unsigned sa_off = static_cast<unsigned>(sa_r * groups);
+  const unsigned sa_off = static_cast<unsigned>(sa_r * gstride);
   int64_t wblock = n0 + TN * wave_n;
   wblock = wblock < n ? wblock : n - 1;
-  const float* sw_src = ws + (wblock >> 7) * groups;
+  const float* sw_src = ws + (wblock >> 7) * gstride + g_lo;
 
   auto stage_base = [&](auto st) -> unsigned char* {
     if constexpr (decltype(st)::value == 0) return lds0;
@@ -343,7 +355,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Epilogue: lane holds, per sub-tile, weight rows 4 (l / 16) .. +3 of token
-  // l % 16: four consecutive outputs in C's row.
+  // l % 16: four consecutive outputs in C's row (or in the partial tile's).
+  if (part != nullptr) {
+    float* pdst = part + ks * m_rows * n;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t m = m0 + TM * wave_m + 16 * j + lrow;
+      if (m >= m_rows) continue;
+#pragma unroll
+      for (int i = 0; i < I; ++i) {
+        const int64_t col = n0 + TN * wave_n + 16 * i + 4 * quarter;
+        float* dst = pdst + m * n + col;
+        const v4f v = acc[i][j];
+        if ((n & 3) == 0 && col + 3 < n) {
+          *reinterpret_cast<v4f*>(dst) = v;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < n) dst[e] = v[e];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int64_t m = m0 + TM * wave_m + 16 * j + lrow;

@@ -15,8 +15,24 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
                               const void* wq, const float* ws, void* c, hipStream_t stream);
 
 // LDS-tiled MFMA kernel, any m >= 1. shape -1 picks the tile shape from
-// (m, n) (tiled_shape); 0..3 force 128x128, 128x256, 192x256, 256x256.
-int tiled_shape(int64_t m, int64_t n);
+// (m, n) (tiled_shape); 0..6 force 128x128, 128x256, 192x256, 256x256,
+// 64x128, 128x64, 64x64. tiled_shape also returns the chosen shape's cost
+// of one K step (1/100 us) through step_cost when that is not null.
+int tiled_shape(int64_t m, int64_t n, int64_t* step_cost);
+
+// K-split tiled path (fp8bq_gemm_ws): shape as above (one of the
+// gemm_tiled_kernel shapes 0, 1, 4, 5, 6) and split > 1 parts of the K
+// groups per tile, or shape = tiled_shape(m, n) and split = 1 (no split);
+// cost in 1/100 us. launch_gemm_split needs part = split x m x n fp32
+// (16-byte aligned) and runs the partial tiles, then their fixed-order sum.
+struct SplitPlan {
+  int shape = 0;
+  int split = 1;
+  int64_t cost = 0;
+};
+SplitPlan split_plan(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_split(int64_t m, int64_t n, int64_t k, const void* aq, const float* as, const void* wq,
+                             const float* ws, void* c, float* part, int shape, int split, hipStream_t stream);
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                              const void* wq, const float* ws, void* c, hipStream_t stream, int shape = -1);
 

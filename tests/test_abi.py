@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert _declared() == {"fp8bq_quant_act", "fp8bq_quant_weight", "fp8bq_gemm", "fp8bq_gemm_path",
-                           "fp8bq_gemm_forced", "fp8bq_gemm_tile_shape", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16",
+                           "fp8bq_gemm_forced", "fp8bq_gemm_workspace_bytes", "fp8bq_gemm_ws", "fp8bq_gemm_ws_forced", "fp8bq_gemm_tile_shape", "fp8bq_gemm_fused", "fp8bq_gemm_w8a16",
                            "fp8bq_topk_workspace_bytes",
                            "fp8bq_topk_bf16", "fp8bq_topk_bf16_noalloc", "fp8bq_rescore_bf16", "fp8bq_mb_read", "fp8bq_mb_empty",
                            "fp8bq_mb_mfma_e4m3", "fp8bq_mb_mfma_e4m3_data", "fp8bq_mb_mfma_e4m3_scaled",
@@ -219,6 +219,55 @@ def test_rescore_errors(fp8bq):
     assert L.fp8bq_rescore_bf16(1, 64, 100, 4, p, p, p, p, p + 2, None) == -3
 
 
+def test_gemm_workspace_plan(fp8bq):
+    # host-only: the K-split plan of fp8bq_gemm_ws (split x M x N x 4 bytes)
+    L = fp8bq.lib()
+    assert L.fp8bq_gemm_workspace_bytes(0, 17408, 5120) == 0
+    assert L.fp8bq_gemm_workspace_bytes(64, 17408, 5120) == 0  # streamed, no tiles
+    assert L.fp8bq_gemm_workspace_bytes(65, 17408, 5120) % (65 * 17408 * 4) == 0
+    for n, k in ((17408, 5120), (5120, 3072), (5120, 8704), (7168, 5120), (8192, 5120)):
+        splits = []
+        for m in (81, 96, 128):
+            b = L.fp8bq_gemm_workspace_bytes(m, n, k)
+            assert b >= 0 and b % (4 * m * n) == 0 and b // (4 * m * n) <= 64, (m, n, k, b)
+            splits.append(b // (4 * m * n))
+        # few tiles: some of these token counts split, except where the 24
+        # groups of K = 3072 leave too little K per part
+        assert (max(splits) >= 2) == (k > 3072), (n, k, splits)
+        for m in range(1, 65, 7):
+            assert L.fp8bq_gemm_workspace_bytes(m, n, k) == 0
+    # a prefill-sized grid fills the CUs without splitting
+    assert L.fp8bq_gemm_workspace_bytes(3465, 17408, 5120) == 0
+    assert L.fp8bq_gemm_workspace_bytes(100, 4096, 128) == 0  # one group: nothing to split
+    assert L.fp8bq_gemm_workspace_bytes(-1, 4, 128) == -2
+    assert L.fp8bq_gemm_workspace_bytes(1, 4, 100) == -2
+
+
+def test_gemm_ws_argument_errors(fp8bq):
+    L = fp8bq.lib()
+    p = FAKE
+    # the workspace: negative size, NULL with a size, misaligned
+    assert L.fp8bq_gemm_ws(100, 4096, 1024, p, p, p, p, p, p, -1, None) == -2
+    assert L.fp8bq_gemm_ws(100, 4096, 1024, p, p, p, p, p, None, 64, None) == -1
+    assert L.fp8bq_gemm_ws(100, 4096, 1024, p, p, p, p, p, p + 8, 64, None) == -3
+    # the GEMM's own checks come first
+    assert L.fp8bq_gemm_ws(100, 4096, 1000, p, p, p, p, p, p, 64, None) == -2
+    assert L.fp8bq_gemm_ws(100, 4096, 1024, None, p, p, p, p, p, 64, None) == -1
+    assert L.fp8bq_gemm_ws(0, 4096, 1024, p, p, p, p, p, None, 0, None) == 0
+    # forced plans: only the gemm_tiled_kernel shapes split, 2..min(64, K/128) parts, enough workspace
+    big = 64 * 100 * 4096 * 4
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_192x256, 2, 100, 4096, 1024, p, p, p, p, p, p, big, None) == -2
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_256x256, 2, 100, 4096, 1024, p, p, p, p, p, p, big, None) == -2
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_STREAM, 2, 100, 4096, 1024, p, p, p, p, p, p, big, None) == -2
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_128x128, 9, 100, 4096, 1024, p, p, p, p, p, p, big, None) == -2
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_128x128, 0, 100, 4096, 1024, p, p, p, p, p, p, big, None) == -2
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_128x128, 65, 100, 4096, 65 * 128, p, p, p, p, p, p, big,
+                                  None) == -2
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_64x64, 3, 100, 4096, 1024, p, p, p, p, p, p,
+                                  3 * 100 * 4096 * 4 - 1, None) == -2
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_64x64, 3, 100, 4096, 1024, p, p, p, p, p, None, 64, None) == -1
+
+
 def test_gemm_path_dispatch_by_explicit_m_ranges(fp8bq):
     L = fp8bq.lib()
     assert L.fp8bq_gemm_path(0, 17408, 5120) == fp8bq.PATH_NONE
@@ -247,6 +296,9 @@ def test_device_error_without_gpu(fp8bq):
     L = fp8bq.lib()
     p = FAKE
     assert L.fp8bq_gemm(1, 4, 128, p, p, p, p, p, None) == -4
+    assert L.fp8bq_gemm_ws(1, 4, 128, p, p, p, p, p, None, 0, None) == -4
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_64x64, 2, 100, 4096, 1024, p, p, p, p, p, p,
+                                  2 * 100 * 4096 * 4, None) == -4
     assert L.fp8bq_quant_act(1, 128, p, p, p, None) == -4
     assert L.fp8bq_gemm_w8a16(1, 4, 128, p, p, p, p, None) == -4
     assert L.fp8bq_gemm_fused(1, 4, 128, p, p, p, p, None) == -4
