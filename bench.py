@@ -380,15 +380,17 @@ def two_stage(reps=50):
     return out
 
 
-SWEEP_M = [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 33, 48, 64, 65, 96, 128, 129, 192, 256, 384, 512, 1024,
-           2048, 3465, 4096]
+SWEEP_M = [1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 17, 24, 32, 33, 48, 49, 64, 65, 80, 81, 96, 128, 129, 192, 256, 384,
+           512, 1024, 2048, 3465, 4096]
 
 
 def m_sweep():
     """fp8bq_gemm over an M grid on the five logged shapes: microseconds per
     call (HIP events on the launch stream, weights rotating over >= 1 GiB of
-    copies), GB/s of algorithmic bytes and TFLOP/s. The dispatch boundaries
-    (8/9, 16/17, 32/33, 64/65, 128/129) are in the grid on purpose."""
+    copies), GB/s of algorithmic bytes and TFLOP/s; where fp8bq_gemm_ws
+    splits K (fp8bq_gemm_workspace_bytes > 0) also its time with the
+    workspace. The dispatch boundaries (8/9, 16/17, 32/33, 48/49, 64/65,
+    80/81, 128/129) are in the grid on purpose."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     s = ctypes.c_void_p(stream.cuda_stream)
@@ -408,12 +410,10 @@ def m_sweep():
         a = torch.randn((mmax, k), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         aq, as_ = fp8bq.quant_act(a)
         c = torch.empty((mmax, n), dtype=torch.bfloat16, device=dev)
-        for m in SWEEP_M:
-            def call(i):
-                wq, wsc = ws[i % copies]
-                st = L.fp8bq_gemm(m, n, k, aq.data_ptr(), as_.data_ptr(), wq.data_ptr(), wsc.data_ptr(), c.data_ptr(), s)
-                if st:
-                    raise fp8bq.Fp8bqError("fp8bq_gemm", st)
+        wbytes = {m: L.fp8bq_gemm_workspace_bytes(m, n, k) for m in SWEEP_M}
+        work = torch.empty(max(16, max(wbytes.values())), dtype=torch.uint8, device=dev)
+
+        def timed(call, m):
             reps = 8 * copies if m <= 256 else 12
             for i in range(reps):
                 call(i)
@@ -424,15 +424,35 @@ def m_sweep():
                 call(i)
             e1.record(stream)
             e1.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / reps
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        for m in SWEEP_M:
+            def call(i):
+                wq, wsc = ws[i % copies]
+                st = L.fp8bq_gemm(m, n, k, aq.data_ptr(), as_.data_ptr(), wq.data_ptr(), wsc.data_ptr(), c.data_ptr(), s)
+                if st:
+                    raise fp8bq.Fp8bqError("fp8bq_gemm", st)
+
+            def call_ws(i):
+                wq, wsc = ws[i % copies]
+                st = L.fp8bq_gemm_ws(m, n, k, aq.data_ptr(), as_.data_ptr(), wq.data_ptr(), wsc.data_ptr(), c.data_ptr(),
+                                     work.data_ptr(), work.numel(), s)
+                if st:
+                    raise fp8bq.Fp8bqError("fp8bq_gemm_ws", st)
+            us = timed(call, m)
             path = L.fp8bq_gemm_path(m, n, k)
             if path == fp8bq.PATH_TILED:
                 path = L.fp8bq_gemm_tile_shape(m, n, k)
-            rows.append({"N": n, "K": k, "M": m, "path": fp8bq.PATH_NAMES[path],
-                         "us": round(us, 2), "GBps": round(gemm_bytes(m, n, k) / (us * 1e-6) / 1e9, 1),
-                         "TFLOPs": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)})
-            print(f"bench: sweep N={n} K={k} M={m}: {us:.2f} us", file=sys.stderr, flush=True)
-        del ws, a, aq, as_, c
+            row = {"N": n, "K": k, "M": m, "path": fp8bq.PATH_NAMES[path],
+                   "us": round(us, 2), "GBps": round(gemm_bytes(m, n, k) / (us * 1e-6) / 1e9, 1),
+                   "TFLOPs": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}
+            if wbytes[m] > 0:  # fp8bq_gemm_ws splits K here: its time and number of K parts
+                row["ws_us"] = round(timed(call_ws, m), 2)
+                row["ws_k_parts"] = wbytes[m] // (4 * m * n)
+            rows.append(row)
+            print(f"bench: sweep N={n} K={k} M={m}: {us:.2f} us" +
+                  (f", with workspace {row['ws_us']:.2f} us" if "ws_us" in row else ""), file=sys.stderr, flush=True)
+        del ws, a, aq, as_, c, work
         torch.cuda.empty_cache()
     return rows
 

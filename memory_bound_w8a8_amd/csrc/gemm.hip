@@ -129,17 +129,30 @@ hipError_t stream_instance(const GemmArgs& a) {
 // C = bf16_rne(part[0] + part[1] + ... + part[split - 1]) elementwise, the
 // parts added in that order (deterministic): the K-split tiled path's second
 // launch. count = M * N; four outputs per thread when count % 4 == 0 (part
-// and c 16-byte aligned).
+// and c 16-byte aligned). S > 0: the number of parts as a compile-time
+// constant (all S loads in flight together); S = 0: any `split`.
+template <int S>
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int split, int64_t count,
                                                            unsigned short* __restrict__ c) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
   const int64_t first = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int parts = S > 0 ? S : split;
   if ((count & 3) == 0) {
     const v4f* p = reinterpret_cast<const v4f*>(part);
     const int64_t q4 = count >> 2;
     for (int64_t q = first; q < q4; q += stride) {
-      v4f sum = p[q];
-      for (int s = 1; s < split; ++s) sum += p[s * q4 + q];
+      v4f sum;
+      if constexpr (S > 0) {
+        v4f t[S];
+#pragma unroll
+        for (int u = 0; u < S; ++u) t[u] = __builtin_nontemporal_load(p + u * q4 + q);
+        sum = t[0];
+#pragma unroll
+        for (int u = 1; u < S; ++u) sum += t[u];
+      } else {
+        sum = p[q];
+        for (int u = 1; u < parts; ++u) sum += __builtin_nontemporal_load(p + u * q4 + q);
+      }
       v2u packed;
       packed[0] = pack_bf16x2(sum[0], sum[1]);
       packed[1] = pack_bf16x2(sum[2], sum[3]);
@@ -148,11 +161,19 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   } else {
     for (int64_t i = first; i < count; i += stride) {
       float sum = part[i];
-      for (int s = 1; s < split; ++s) sum += part[s * count + i];
+      for (int u = 1; u < parts; ++u) sum += part[u * count + i];
       c[i] = static_cast<unsigned short>(pack_bf16x2(sum, 0.f) & 0xffffu);
     }
   }
 }
+
+template <int... S>
+constexpr std::array<void (*)(const float*, int, int64_t, unsigned short*), sizeof...(S)> reduce_table(
+    std::integer_sequence<int, S...>) {
+  return {&split_reduce_kernel<S>...};
+}
+// split_reduce_kernel<S> for S = 0 (any split) .. 16
+constexpr auto kSplitReduce = reduce_table(std::make_integer_sequence<int, 17>{});
 
 __global__ void fill_zero_kernel(unsigned short* __restrict__ c, int64_t count) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -434,8 +455,9 @@ hipError_t launch_gemm_split(int64_t m, int64_t n, int64_t k, const void* aq, co
   const int64_t per = (count & 3) == 0 ? count / 4 : count;
   int64_t blocks = (per + 255) / 256;
   blocks = blocks < 2048 ? blocks : 2048;
-  hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, part, split,
-                     count, static_cast<unsigned short*>(c));
+  hipLaunchKernelGGL(kSplitReduce[split < static_cast<int>(kSplitReduce.size()) ? split : 0],
+                     dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, part, split, count,
+                     static_cast<unsigned short*>(c));
   return hipGetLastError();
 }
 
