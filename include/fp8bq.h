@@ -174,8 +174,9 @@ int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_f
  * agree with the fp64 definition within fp32 accumulation plus bf16
  * rounding).
  *   workspace        device memory, 16-B aligned, workspace_bytes long (NULL
- *                    only with workspace_bytes == 0); overwritten. Calls
- *                    sharing a workspace must be ordered (same stream).
+ *                    only with workspace_bytes == 0), not overlapping the
+ *                    other arguments; overwritten. Calls sharing a
+ *                    workspace must be ordered (same stream).
  *   workspace_bytes  >= fp8bq_gemm_workspace_bytes(M, N, K) > 0: the split
  *                    plan runs; otherwise exactly fp8bq_gemm's kernels run
  *                    (bitwise equal to fp8bq_gemm).
@@ -192,7 +193,7 @@ int fp8bq_gemm_forced(int path, int64_t M, int64_t N, int64_t K, const void *A_f
  * and the number of K parts (2 .. min(64, K/128)) forced, workspace_bytes
  * >= split x M x N x 4; split == 1 runs fp8bq_gemm_forced(path, ...). For
  * cross-checking plans: FP8BQ_ERR_SHAPE for a shape or split it cannot
- * run.
+ * run, or a grid of tiles x split workgroups of 2^31 or more.
  */
 int64_t fp8bq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int fp8bq_gemm_ws(int64_t M, int64_t N, int64_t K, const void *A_fp8, const float *A_scales,

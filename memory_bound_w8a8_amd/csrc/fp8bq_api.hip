@@ -199,6 +199,8 @@ int fp8bq_gemm_ws_forced(int path, int split, int64_t M, int64_t N, int64_t K, c
   const bool splits = shape == 0 || shape == 1 || shape == 4 || shape == 5 || shape == 6;
   if (!splits || split < 2 || split > 64 || split > K / 128 || K >= kTiledMaxK) return FP8BQ_ERR_SHAPE;
   if (M == 0 || N == 0) return FP8BQ_OK;
+  // the grid, tiles x split workgroups, must stay within 2^31
+  if (fp8bq::tile_grid(M, N, shape) * split >= (int64_t(1) << 31)) return FP8BQ_ERR_SHAPE;
   if (workspace_bytes < split * M * N * 4) return FP8BQ_ERR_SHAPE;
   st = check_device();
   if (st != FP8BQ_OK) return st;

@@ -404,6 +404,10 @@ constexpr int64_t kUnsplitPerMille = 1146;
 constexpr int64_t kUnsplitOffset = -178;
 constexpr int kMaxSplit = 64;
 
+int64_t tile_grid(int64_t m, int64_t n, int shape) {
+  return shape >= 0 && shape < kNumTileShapes ? tile_count(m, n, kTileShapes[shape]) : 0;
+}
+
 SplitPlan split_plan(int64_t m, int64_t n, int64_t k) {
   SplitPlan plan;
   const int64_t groups = k / kGroup;

@@ -31,6 +31,8 @@ struct SplitPlan {
   int64_t cost = 0;
 };
 SplitPlan split_plan(int64_t m, int64_t n, int64_t k);
+// Tiles of tile shape `shape` (0..6, as for launch_gemm_tiled) over M x N.
+int64_t tile_grid(int64_t m, int64_t n, int shape);
 hipError_t launch_gemm_split(int64_t m, int64_t n, int64_t k, const void* aq, const float* as, const void* wq,
                              const float* ws, void* c, float* part, int shape, int split, hipStream_t stream);
 hipError_t launch_gemm_tiled(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,

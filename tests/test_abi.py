@@ -266,6 +266,10 @@ def test_gemm_ws_argument_errors(fp8bq):
     assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_64x64, 3, 100, 4096, 1024, p, p, p, p, p, p,
                                   3 * 100 * 4096 * 4 - 1, None) == -2
     assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_64x64, 3, 100, 4096, 1024, p, p, p, p, p, None, 64, None) == -1
+    # a grid of 2^31 or more workgroups: (2^20 / 64)^2 tiles of 64 x 64 in 8 parts
+    big_mn = 1 << 20
+    assert L.fp8bq_gemm_ws_forced(fp8bq.PATH_TILED_64x64, 8, big_mn, big_mn, 1024, p, p, p, p, p, p, 1 << 62,
+                                  None) == -2
 
 
 def test_gemm_path_dispatch_by_explicit_m_ranges(fp8bq):
