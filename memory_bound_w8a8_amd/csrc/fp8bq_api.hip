@@ -11,8 +11,9 @@
 namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 40;  // bound on M*K, N*K, M*N
-constexpr int64_t kStreamMaxM = 64;              // streaming kernels serve 1..64 tokens per launch
-constexpr int64_t kStreamSplitMaxM = 128;        // forced streaming path: 65..128 as two launches (64 + the rest)
+constexpr int64_t kStreamMaxM = 64;              // streaming kernels: 1..64 tokens per launch on any shape
+constexpr int64_t kStreamSplitMaxM = 128;        // forced streaming path up to 128 tokens (two launches past 64
+                                                 // where the 65..80 instances do not serve)
 constexpr int64_t kTiledMaxK = int64_t(1) << 24; // tiled kernel: 32-bit offsets within a 256-row tile
 constexpr int kMaxDevices = 64;
 constexpr int64_t kSmallMaxM = 16;               // weight-only path: one 16-token tile

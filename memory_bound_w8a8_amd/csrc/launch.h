@@ -10,7 +10,8 @@ namespace fp8bq {
 hipError_t launch_quant_act(int64_t m, int64_t k, const void* a, void* aq, float* as, hipStream_t stream);
 hipError_t launch_quant_weight(int64_t n, int64_t k, const float* w, void* wq, float* ws, hipStream_t stream);
 
-// Weight-streaming split-K kernel, 1 <= m <= 64.
+// Weight-streaming split-K kernel, 1 <= m <= 64, and 65 <= m <= 80 where
+// stream_wide_serves(m, n, k) (hipErrorInvalidValue otherwise).
 hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, const float* as,
                               const void* wq, const float* ws, void* c, hipStream_t stream);
 
