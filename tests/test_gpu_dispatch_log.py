@@ -28,6 +28,10 @@ w_q, w_s = fp8bq.quant_weight(torch.randn(8192, k, device=dev) * 0.02)
 for m in (80, 81):
     a_q, a_s = fp8bq.quant_act(torch.randn(m, k, device=dev).to(torch.bfloat16))
     fp8bq.gemm(a_q, a_s, w_q, w_s)
+# with a workspace, 65..~256 tokens split K where the cost model says so
+w_q, w_s = fp8bq.quant_weight(torch.randn(5120, 8704, device=dev) * 0.02)
+a_q, a_s = fp8bq.quant_act(torch.randn(96, 8704, device=dev).to(torch.bfloat16))
+fp8bq.gemm_ws(a_q, a_s, w_q, w_s)
 # tile shapes by rounds x step cost on (5120, 8704): 192 x 256 at the prefill size,
 # 128 x 256 where it keeps the grid within the same rounds
 w_q, w_s = fp8bq.quant_weight(torch.randn(5120, 8704, device=dev) * 0.02)
@@ -56,6 +60,8 @@ def test_dispatch_log_names_each_decision_once():
     assert got["fp8bq: gemm(stream) M=80 N=8192 K=5120"] == (
         "gemm_rows64_kernel MS=5 TILES=2 GMAX=5 rows/wg=32 grid=256")
     assert got["fp8bq: gemm(tiled) M=81 N=8192 K=5120"].startswith("gemm_tiled")
+    ws_line = got["fp8bq: gemm(tiled, split K) M=96 N=5120 K=8704"]
+    assert ws_line.startswith("gemm_tiled_kernel BM=") and " parts) + split_reduce_kernel" in ws_line
     assert got["fp8bq: gemm_fused M=2 N=17408 K=5120"].startswith("gemm_rows_kernel MT=16 act=bf16 TOK=2")
     # 380 tiles of 192 x 256 (one round, then the last 124 tiles as 248 column halves in about half a
     # round) beat 280 of 256 x 256 (one round + 48 halves) and 560 of 128 x 256 (2.19 rounds)
