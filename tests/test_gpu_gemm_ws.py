@@ -32,18 +32,33 @@ def _problem(m, n, k):
 
 
 # Every tile shape that splits, K parts of unequal length (9 groups in 2, 4
-# and 7 parts), ragged M and N (partial token and weight tiles).
+# and 7 parts), ragged M and N (partial token and weight tiles); N = 701
+# makes M x N odd, which takes the partial tiles' and the reduction's
+# one-output-at-a-time paths.
 @pytest.mark.parametrize("path", SPLIT_PATHS)
 @pytest.mark.parametrize("split", [2, 4, 7])
-def test_forced_split_whole_output_and_repeatable(path, split):
-    m, n, k = 70, 700, 1152
+@pytest.mark.parametrize("n", [700, 701])
+def test_forced_split_whole_output_and_repeatable(path, split, n):
+    m, k = 70, 1152
     a_q, a_s, w_q, w_s = _problem(m, n, k)
     args = [to_gpu(x) for x in (a_q, a_s, w_q, w_s)]
     c = fp8bq.gemm_ws_forced(path, split, *args)
     c2 = fp8bq.gemm_ws_forced(path, split, *args)
     torch.cuda.synchronize()
     assert torch.equal(c.view(torch.int16), c2.view(torch.int16))
-    assert_gemm_close(bf16_to_f64(c), gemm_ref(a_q, a_s, w_q, w_s), what=f"path {path} split {split}")
+    assert_gemm_close(bf16_to_f64(c), gemm_ref(a_q, a_s, w_q, w_s), what=f"path {path} split {split} N {n}")
+
+
+# More parts than the reduction's compile-time instances (up to 16): the
+# generic any-count path, 40 groups in 20 and 40 parts.
+@pytest.mark.parametrize("split", [20, 40])
+def test_forced_split_many_parts(split):
+    m, n, k = 65, 640, 5120
+    a_q, a_s, w_q, w_s = _problem(m, n, k)
+    args = [to_gpu(x) for x in (a_q, a_s, w_q, w_s)]
+    c = fp8bq.gemm_ws_forced(fp8bq.PATH_TILED_64x64, split, *args)
+    torch.cuda.synchronize()
+    assert_gemm_close(bf16_to_f64(c), gemm_ref(a_q, a_s, w_q, w_s), what=f"split {split}")
 
 
 # |codes| <= 8, scales in {1/2, 1, 2}, K = 1024: every product, group sum,
