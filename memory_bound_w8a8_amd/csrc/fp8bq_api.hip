@@ -105,8 +105,12 @@ int run_gemm(int path, int64_t M, int64_t N, int64_t K, const void* A_fp8, const
 
 // Workspace bytes the K-split plan of fp8bq_gemm_ws needs for a valid
 // (M, N, K) with M, N, K > 0 (0 when the plan does not split).
+// Beyond the streaming kernels' reach the plan competes with the unsplit
+// tiled plan; at 33..64 tokens it replaces streaming only where that is
+// bound by long per-wave K ranges (stream_deep_k).
 int64_t split_workspace_bytes(int64_t M, int64_t N, int64_t K, fp8bq::SplitPlan* plan) {
-  if (gemm_path(M, N, K) != FP8BQ_PATH_TILED || K >= kTiledMaxK) return 0;
+  if (K >= kTiledMaxK) return 0;
+  if (gemm_path(M, N, K) != FP8BQ_PATH_TILED && !fp8bq::stream_deep_k(M, N, K)) return 0;
   *plan = fp8bq::split_plan(M, N, K);
   return plan->split > 1 ? plan->split * M * N * 4 : 0;
 }

@@ -234,8 +234,12 @@ def test_gemm_workspace_plan(fp8bq):
         # few tiles: some of these token counts split, except where the 24
         # groups of K = 3072 leave too little K per part
         assert (max(splits) >= 2) == (k > 3072), (n, k, splits)
-        for m in range(1, 65, 7):
+        for m in range(1, 33, 3):
             assert L.fp8bq_gemm_workspace_bytes(m, n, k) == 0
+        # 33..64 tokens split only where the streaming waves walk 8..9 groups
+        # over at most 2 row tiles (K = 8704 here)
+        for m in (33, 48, 64):
+            assert (L.fp8bq_gemm_workspace_bytes(m, n, k) > 0) == (k == 8704), (m, n, k)
     # a prefill-sized grid fills the CUs without splitting
     assert L.fp8bq_gemm_workspace_bytes(3465, 17408, 5120) == 0
     assert L.fp8bq_gemm_workspace_bytes(100, 4096, 128) == 0  # one group: nothing to split

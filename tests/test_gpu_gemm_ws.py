@@ -92,18 +92,20 @@ def test_without_enough_workspace_it_is_the_plain_gemm():
     c_small = fp8bq.gemm_ws(a_q, a_s, w_q, w_s, workspace=small)
     torch.cuda.synchronize()
     assert torch.equal(c_small.view(torch.int16), c.view(torch.int16))
-    # up to 64 tokens there is no split plan and no workspace is read
-    assert fp8bq.gemm_workspace_bytes(64, n, k) == 0
-    c64 = fp8bq.gemm_ws(a_q[:64], a_s[:64], w_q, w_s)
+    # up to 32 tokens there is no split plan and no workspace is read
+    assert fp8bq.gemm_workspace_bytes(32, n, k) == 0
+    c32 = fp8bq.gemm_ws(a_q[:32], a_s[:32], w_q, w_s)
     torch.cuda.synchronize()
-    assert torch.equal(c64.view(torch.int16), fp8bq.gemm(a_q[:64], a_s[:64], w_q, w_s).view(torch.int16))
+    assert torch.equal(c32.view(torch.int16), fp8bq.gemm(a_q[:32], a_s[:32], w_q, w_s).view(torch.int16))
 
 
 # The default plan at the logged shapes' full sizes, 65..256 tokens (the
-# counts whose tiles leave CUs idle): A and W quantised on the GPU (checked
+# counts whose tiles leave CUs idle) and 33..64 on (5120, 8704), where the
+# split replaces streaming: A and W quantised on the GPU (checked
 # bit for bit against the oracle on the sampled rows and row blocks), then
 # sampled outputs against the oracle.
 WS_CASES = [(m, n, k) for n, k in workloads.SHAPES for m in (65, 80, 96, 128, 200, 256)]
+WS_CASES += [(m, 5120, 8704) for m in (33, 48, 64)]  # deep K: the split replaces streaming
 
 
 @pytest.fixture(scope="module")
