@@ -217,7 +217,8 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
 }
 
 // 33..64 tokens where each wave of the streaming kernel walks a long K
-// range (8 or 9 groups) over a short row range (at most 2 row tiles): there
+// range (8 or 9 groups) over a short row range (2 row tiles, N = 4097..8192;
+// a single row tile was not measured): there
 // the wave's serial chain, not HBM, sets the streaming time, and the
 // K-split tiled plan of fp8bq_gemm_ws measured faster: on (5120, 8704)
 // 16.1 / 17.5 us against 19.7 / 23.8 at M = 48 / 64 (64 x 128 tiles in 6
@@ -225,7 +226,7 @@ hipError_t launch_gemm_stream(int64_t m, int64_t n, int64_t k, const void* aq, c
 bool stream_deep_k(int64_t m, int64_t n, int64_t k) {
   int64_t rows_per_wg;
   int tiles, gmax;
-  return m > 32 && m <= 64 && rows_shape(n, k, &rows_per_wg, &tiles, &gmax) && tiles <= 2 && gmax >= 8;
+  return m > 32 && m <= 64 && rows_shape(n, k, &rows_per_wg, &tiles, &gmax) && tiles == 2 && gmax >= 8;
 }
 
 bool stream_wide_serves(int64_t m, int64_t n, int64_t k) {

@@ -46,7 +46,7 @@ bool small_m_supported(int64_t m, int64_t n, int64_t k);
 // 16-row tiles per workgroup).
 bool stream_wide_serves(int64_t m, int64_t n, int64_t k);
 // Whether 33..64 tokens on (N, K) stream with long per-wave K ranges (8..9
-// groups) over at most 2 row tiles, where fp8bq_gemm_ws splits K instead.
+// groups) over 2 row tiles, where fp8bq_gemm_ws splits K instead.
 bool stream_deep_k(int64_t m, int64_t n, int64_t k);
 
 // Activation quantisation fused into the streaming GEMM (bf16 activation in).
