@@ -662,17 +662,18 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(rows=4096, runs=5):
-    """The CPU oracle (numpy, fp64 GEMM) on a bounded sample of the workload:
-    activation quantisation (quant_act_ref) and the GEMM (gemm_ref) for
-    M = 1..8 against the first `rows` weight rows of (N, K) = (17408, 5120),
-    the weight pre-quantised. One warm-up pass, then the median of `runs`
-    passes, with the host's threads (all cores this process may use, at most
-    the OMP_NUM_THREADS share when that is set) and with one thread. Also the
-    plain fp64 matmul alone on pre-dequantised operands (the oracle's
-    arithmetic without its decode and per-group loop). Reported in GB/s of the
-    same algorithmic bytes as the GPU figure, and as us per call scaled to the
-    full N."""
+def cpu_baseline(rows=N, runs=5, runs_one_thread=3):
+    """The CPU oracle (numpy, fp64 GEMM) on the workload: activation
+    quantisation (quant_act_ref) and the GEMM (gemm_ref) for M = 1..8
+    against the first `rows` weight rows of (N, K) = (17408, 5120) (all of
+    them by default: about 20 s of CPU work on a 16-thread host), the weight
+    pre-quantised. One warm-up pass, then the median of `runs` passes with
+    the host's threads (all cores this process may use, at most the
+    OMP_NUM_THREADS share when that is set) and of `runs_one_thread` passes
+    with one thread. Also the plain fp64 matmul alone on pre-dequantised
+    operands (the oracle's arithmetic without its decode and per-group loop).
+    Reported in GB/s of the same algorithmic bytes as the GPU figure, and as
+    us per call over the full N."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import e4m3_decode, gemm_ref, quant_act_ref, quant_weight_ref
@@ -694,9 +695,9 @@ def cpu_baseline(rows=4096, runs=5):
             gemm_ref(a_q, a_s, w_q, w_s)
         return time.perf_counter() - t0
 
-    def median_pass():
+    def median_pass(count):
         one_pass()
-        return float(np.median([one_pass() for _ in range(runs)]))
+        return float(np.median([one_pass() for _ in range(count)]))
 
     # the same sums with operands already decoded and scaled, one fp64 matmul per M
     w_deq = e4m3_decode(w_q) * np.repeat(np.repeat(w_s.astype(np.float64), 128, axis=0)[:rows], 128, axis=1)
@@ -713,11 +714,11 @@ def cpu_baseline(rows=4096, runs=5):
 
     with threadpool_limits(limits=cores):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        t_all = median_pass()
+        t_all = median_pass(runs)
         matmul_pass()
         t_mm = float(np.median([matmul_pass() for _ in range(runs)]))
     with threadpool_limits(limits=1):
-        t_one = median_pass()
+        t_one = median_pass(runs_one_thread)
     scale = N / rows  # calls over the full weight take N / rows times the sample
     return {
         "value": round(sample_bytes / t_all / 1e9, 4),
@@ -725,11 +726,13 @@ def cpu_baseline(rows=4096, runs=5):
         "cores": used,
         "kind": "oracle",
         "cpu_model": cpu_model(),
-        "sample": f"quant_act_ref + gemm_ref for M=1..8 on the first {rows} of {N} weight rows (K={K}); "
-                  f"median of {runs} passes after 1 warm-up",
+        "sample": (f"quant_act_ref + gemm_ref for M=1..8 on " +
+                   ("all " if rows == N else f"the first {rows} of ") + f"{N} weight rows (K={K}); median of {runs} "
+                   f"passes after 1 warm-up ({runs_one_thread} with one thread)"),
         "pass_s": round(t_all, 4),
         "us_per_call_full_N": round(t_all / len(MS) * scale * 1e6, 1),
-        "one_thread": {"value": round(sample_bytes / t_one / 1e9, 4), "unit": "GB/s", "pass_s": round(t_one, 4),
+        "one_thread": {"value": round(sample_bytes / t_one / 1e9, 4), "unit": "GB/s", "cores": 1,
+                       "pass_s": round(t_one, 4),
                        "us_per_call_full_N": round(t_one / len(MS) * scale * 1e6, 1)},
         "matmul_only": {"what": "fp64 A_deq @ W_deq.T per M, operands pre-dequantised", "pass_s": round(t_mm, 4),
                         "value": round(sample_bytes / t_mm / 1e9, 4), "unit": "GB/s",
