@@ -534,25 +534,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
     if constexpr (decltype(st)::value == 0) return lds0;
     else return lds1;
   };
-  auto issue = [&](int64_t g, auto st) {
+  // The copies of group g into stage st: this wave's 8-row chunks c = 0 ..
+  // A_CHUNKS - 1 of the token tile, then A_CHUNKS .. CHUNKS - 1 of the
+  // weight tile, and (waves 0 .. BM / 64 - 1) the token scales.
+  constexpr int CHUNKS = A_CHUNKS + W_CHUNKS;
+  auto issue_chunk = [&](int64_t g, auto st, int c) {
     unsigned char* base = stage_base(st);
-    const unsigned char* ag = a_base + g * kGroup;
-    const unsigned char* wg = w_base + g * kGroup;
-#pragma unroll
-    for (int q = 0; q < A_CHUNKS; ++q) {
+    if (c < A_CHUNKS) {
       if constexpr (CLAMP)
-        dma16(ag, a_off[q], base + 1024 * (wave + WAVES * q));
+        dma16(a_base + g * kGroup, a_off[c], base + 1024 * (wave + WAVES * c));
       else
-        dma16(a_chunk[q] + g * kGroup, a_off[0], base + 1024 * (wave + WAVES * q));
-    }
-#pragma unroll
-    for (int q = 0; q < W_CHUNKS; ++q) {
+        dma16(a_chunk[c] + g * kGroup, a_off[0], base + 1024 * (wave + WAVES * c));
+    } else {
+      const int q = c - A_CHUNKS;
       if constexpr (CLAMP)
-        dma16(wg, w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
+        dma16(w_base + g * kGroup, w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
       else
         dma16(w_chunk[q] + g * kGroup, w_off[0], base + BM * 128 + 1024 * (wave + WAVES * q));
     }
-    if (copies_scales) dma4(uniform(sa_base + g), 4 * sa_off, base + (BM + BN) * 128 + 256 * wave);
+  };
+  auto issue_scales = [&](int64_t g, auto st) {
+    if (copies_scales) dma4(uniform(sa_base + g), 4 * sa_off, stage_base(st) + (BM + BN) * 128 + 256 * wave);
+  };
+  auto issue = [&](int64_t g, auto st) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) issue_chunk(g, st, c);
+    issue_scales(g, st);
   };
   auto frag = [&](const unsigned char* base, int r) -> v8i {
     const int x = r & 7;
@@ -641,11 +648,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
       set_prio(3);
+      // step g + 2's copies, spread over the deferred sub-tile's MFMAs
+      // (issued at once after the barrier, every wave's burst of copies
+      // held up its MFMAs: 3.5% more cycles per K step)
       const int64_t g2 = g + 2 < groups ? g + 2 : groups - 1;
-      issue(g2, st);
+      issue_scales(g2, st);
       const v8i af_n = a_frag(SN{}, 0);
       const float sa_n = a_scale(SN{}, 0);
-      mfma_row(J - 2, sa * sw, [&](int i) { wf[i] = w_frag(SN{}, i); });
+      mfma_row(J - 2, sa * sw, [&](int i) {
+        wf[i] = w_frag(SN{}, i);
+#pragma unroll
+        for (int c = i * CHUNKS / I; c < (i + 1) * CHUNKS / I; ++c) issue_chunk(g2, st, c);
+      });
       af = af_n;
       sa = sa_n;
       sw = sw_n;
