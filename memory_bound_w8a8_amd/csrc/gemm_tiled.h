@@ -46,7 +46,8 @@ namespace fp8bq {
 typedef __attribute__((address_space(3))) const void lds_void;
 
 // Direct global -> LDS copies (lane i's bytes land at base + size * i; the
-// LDS base goes through M0 and must be uniform across the wave). Issued as
+// LDS base goes through M0 and must be uniform across the wave, which
+// readfirstlane states to the compiler). Issued as
 // inline assembly so that the compiler does not track them: it cannot tell
 // which stage a copy writes and would otherwise wait for every copy in
 // flight before each LDS read. The kernel orders them itself (explicit
@@ -66,12 +67,12 @@ __device__ __forceinline__ const void* uniform(const void* p) {
 }
 __device__ __forceinline__ void dma16(const void* sbase, unsigned voff, void* lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds_addr(lds_base))
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)))
                : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* sbase, unsigned voff, void* lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds_addr(lds_base))
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_base)))
                : "memory", "m0");
 }
 
@@ -448,9 +449,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
   static_assert(BM % (8 * WAVES) == 0 && BN % (8 * WAVES) == 0, "8-row load chunks spread over the waves");
   static_assert(BM % 64 == 0 && BM <= 64 * WAVES, "scales: one dword per token, 64 tokens per wave");
   static_assert(J >= 2, "at least two token sub-tiles per wave");
-  constexpr int kStageBytes = (BM + BN) * 128 + BM * 4;
+  constexpr int kStageBytes = (BM + BN) * 128;
   __shared__ __attribute__((aligned(16))) unsigned char lds0[kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds1[kStageBytes];
+  // token scales of 8 groups at a time, [token][8], two buffers (groups
+  // 8c .. 8c + 7 in buffer c % 2)
+  __shared__ __attribute__((aligned(16))) float lds_scales[2 * BM * 8];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -498,11 +502,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
     a_off[0] = static_cast<unsigned>(cr * k + 16 * ((lane & 7) ^ cr));
     w_off[0] = a_off[0];
   }
-  const bool copies_scales = wave < BM / 64;
+  // Token scales: every 8 groups, the tile's BM x 8 block, one dword copy
+  // per lane (lane l: token 8 u + l / 8, group 8 c + l % 8 of the wave's
+  // u-th 8-token chunk), so a copy touches 8 rows' lines instead of the 64
+  // of a per-group gather (which cost 4% of the K step).
+  constexpr int S_CHUNKS = BM / 8 / WAVES;
   const float* sa_base = as + m0 * groups;
-  const int sa_t = 64 * (copies_scales ? wave : 0) + lane;
-  const int64_t sa_r = (!CLAMP || m0 + sa_t < m_rows) ? sa_t : m_rows - 1 - m0;
-  const unsigned sa_off = static_cast<unsigned>(sa_r * groups);
   int64_t wblock = n0 + TN * wave_n;
   if (CLAMP) wblock = wblock < n ? wblock : n - 1;
   const float* sw_src = ws + (wblock >> 7) * groups;
@@ -542,24 +547,32 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
     unsigned char* base = stage_base(st);
     if (c < A_CHUNKS) {
       if constexpr (CLAMP)
-        dma16(a_base + g * kGroup, a_off[c], base + 1024 * (wave + WAVES * c));
+        dma16(uniform(a_base + g * kGroup), a_off[c], base + 1024 * (wave + WAVES * c));
       else
         dma16(a_chunk[c] + g * kGroup, a_off[0], base + 1024 * (wave + WAVES * c));
     } else {
       const int q = c - A_CHUNKS;
       if constexpr (CLAMP)
-        dma16(w_base + g * kGroup, w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
+        dma16(uniform(w_base + g * kGroup), w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
       else
         dma16(w_chunk[q] + g * kGroup, w_off[0], base + BM * 128 + 1024 * (wave + WAVES * q));
     }
   };
-  auto issue_scales = [&](int64_t g, auto st) {
-    if (copies_scales) dma4(uniform(sa_base + g), 4 * sa_off, stage_base(st) + (BM + BN) * 128 + 256 * wave);
+  auto issue_scales = [&](int64_t g) {  // g a multiple of 8
+    const int64_t col = g + (lane & 7) < groups ? g + (lane & 7) : groups - 1;
+#pragma unroll
+    for (int q = 0; q < S_CHUNKS; ++q) {
+      const int u = wave + WAVES * q;
+      const int r = 8 * u + cr;
+      const int64_t row = (!CLAMP || m0 + r < m_rows) ? r : m_rows - 1 - m0;
+      dma4(uniform(sa_base), static_cast<unsigned>(4 * (row * groups + col)),
+           reinterpret_cast<unsigned char*>(lds_scales) + 4 * BM * 8 * ((g >> 3) & 1) + 256 * u);
+    }
   };
   auto issue = [&](int64_t g, auto st) {
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) issue_chunk(g, st, c);
-    issue_scales(g, st);
+    if ((g & 7) == 0) issue_scales(g);
   };
   auto frag = [&](const unsigned char* base, int r) -> v8i {
     const int x = r & 7;
@@ -568,8 +581,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
     return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
   auto a_frag = [&](auto st, int j) -> v8i { return frag(stage_base(st), TM * wave_m + 16 * j + lrow); };
-  auto a_scale = [&](auto st, int j) -> float {
-    return reinterpret_cast<const float*>(stage_base(st) + (BM + BN) * 128)[TM * wave_m + 16 * j + lrow];
+  auto a_scale = [&](int64_t g, int j) -> float {
+    return lds_scales[BM * 8 * ((g >> 3) & 1) + 8 * (TM * wave_m + 16 * j + lrow) + (g & 7)];
   };
   auto w_frag = [&](auto st, int i) -> v8i { return frag(stage_base(st) + BM * 128, TN * wave_n + 16 * i + lrow); };
 
@@ -591,7 +604,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
 #pragma unroll
   for (int i = 0; i < I; ++i) wf[i] = w_frag(S0{}, i);
   v8i af = a_frag(S0{}, 0);
-  float sa = a_scale(S0{}, 0);
+  float sa = a_scale(0, 0);
   float sw_lanes = sw_chunk(0);
   float sw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw_lanes), 0));
   // results of the previous token sub-tile awaiting their scale FMA (zeros
@@ -633,7 +646,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
 #pragma unroll
     for (int j = 0; j < J - 1; ++j) {
       const v8i af_n = a_frag(st, j + 1);
-      const float sa_n = a_scale(st, j + 1);
+      const float sa_n = a_scale(g, j + 1);
       set_prio(3 - (3 * (j + 1)) / (J - 1));
       mfma_row((j + J - 1) % J, sa * sw, nothing);
       af = af_n;
@@ -652,9 +665,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
       // (issued at once after the barrier, every wave's burst of copies
       // held up its MFMAs: 3.5% more cycles per K step)
       const int64_t g2 = g + 2 < groups ? g + 2 : groups - 1;
-      issue_scales(g2, st);
+      if (g + 2 < groups && (g2 & 7) == 0) issue_scales(g2);
       const v8i af_n = a_frag(SN{}, 0);
-      const float sa_n = a_scale(SN{}, 0);
+      const float sa_n = a_scale(g + 1, 0);
       mfma_row(J - 2, sa * sw, [&](int i) {
         wf[i] = w_frag(SN{}, i);
 #pragma unroll
