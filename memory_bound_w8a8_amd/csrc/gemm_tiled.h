@@ -83,13 +83,15 @@ struct TiledKernel {
   static constexpr int kTN = BN / WN;  // weight rows per wave
   static constexpr int kJ = kTM / 16;  // token sub-tiles per wave
   static constexpr int kI = kTN / 16;  // weight-row sub-tiles per wave
-  // A codes, W codes, then the BM activation scales (waves 0 .. BM / 64 - 1
-  // copy 64 each; the other waves copy none)
-  static constexpr int kStageBytes = (BM + BN) * 128 + BM * 4;
-  static constexpr int kLdsBytes = STAGES * kStageBytes;
-  // direct-to-LDS loads one wave issues per K step (plus one for the waves
-  // that copy scales)
+  // A codes, then W codes (the activation scales sit in a separate
+  // two-buffer array, 8 groups at a time)
+  static constexpr int kStageBytes = (BM + BN) * 128;
+  static constexpr int kScaleBytes = 2 * BM * 8 * 4;
+  static constexpr int kLdsBytes = STAGES * kStageBytes + kScaleBytes;
+  // direct-to-LDS loads one wave issues per K step (plus kScaleLoadsPerWave
+  // every 8 steps)
   static constexpr int kTileLoadsPerWave = BM / 8 / kWaves + BN / 8 / kWaves;
+  static constexpr int kScaleLoadsPerWave = BM / 8 / kWaves;
 };
 
 // Wait until at most N of this wave's vector-memory operations are
@@ -157,6 +159,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   __shared__ __attribute__((aligned(16))) unsigned char lds0[KC::kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds1[KC::kStageBytes];
   __shared__ __attribute__((aligned(16))) unsigned char lds2[STAGES > 2 ? KC::kStageBytes : 16];
+  // token scales of 8 groups at a time, [token][8], two buffers (groups
+  // 8c .. 8c + 7 of this workgroup's K range in buffer c % 2)
+  __shared__ __attribute__((aligned(16))) float lds_scales[2 * BM * 8];
 
   const int lane = threadIdx.x & 63;
   // wave index as a provably uniform value: per-wave pointers (the weight
@@ -210,14 +215,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
     const int64_t row = n0 + r < n ? r : n - 1 - n0;
     w_off[q] = static_cast<unsigned>(row * k + 16 * ((lane & 7) ^ (r & 7)));
   }
-  // Activation scales of the tile's tokens: wave w < BM / 64 copies tokens
-  // 64 w .. 64 w + 63 (one dword each: a 64-line gather, so only as many
-  // waves as there are distinct slots issue one).
-  const bool copies_scales = wave < BM / 64;
-  const float* sa_base = as + m0 * gstride + g_lo;
-  const int sa_t = 64 * (copies_scales ? wave : 0) + lane;
-  const int64_t sa_r = m0 + sa_t < m_rows ? sa_t : m_rows - 1 - m0;
-  const unsigned sa_off = static_cast<unsigned>(sa_r * gstride);
+  // Activation scales of the tile's tokens: every 8 groups the BM x 8 block,
+  // one dword copy per lane (lane l: token 8 u + l / 8, group 8 c + l % 8 of
+  // the wave's u-th 8-token chunk), so a copy touches 8 rows' lines rather
+  // than the 64 of a per-group gather.
+  constexpr int S_CHUNKS = KC::kScaleLoadsPerWave;
+  const float* sa_base = as + m0 * gstride;
   int64_t wblock = n0 + TN * wave_n;
   wblock = wblock < n ? wblock : n - 1;
   const float* sw_src = ws + (wblock >> 7) * gstride + g_lo;
@@ -230,13 +233,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
 
   auto issue = [&](int64_t g, auto st) {
     unsigned char* base = stage_base(st);
-    const unsigned char* ag = a_base + g * kGroup;
-    const unsigned char* wg = w_base + g * kGroup;
+    const void* ag = uniform(a_base + g * kGroup);
+    const void* wg = uniform(w_base + g * kGroup);
 #pragma unroll
     for (int q = 0; q < A_CHUNKS; ++q) dma16(ag, a_off[q], base + 1024 * (wave + WAVES * q));
 #pragma unroll
     for (int q = 0; q < W_CHUNKS; ++q) dma16(wg, w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
-    if (copies_scales) dma4(uniform(sa_base + g), 4 * sa_off, base + (BM + BN) * 128 + 256 * wave);
+    if ((g & 7) == 0) {  // the scales of groups g .. g + 7
+      const int64_t col = g_lo + g + (lane & 7) < gstride ? g_lo + g + (lane & 7) : gstride - 1;
+#pragma unroll
+      for (int q = 0; q < S_CHUNKS; ++q) {
+        const int u = wave + WAVES * q;
+        const int r = 8 * u + cr;
+        const int64_t row = m0 + r < m_rows ? r : m_rows - 1 - m0;
+        dma4(uniform(sa_base), static_cast<unsigned>(4 * (row * gstride + col)),
+             reinterpret_cast<unsigned char*>(lds_scales) + 4 * BM * 8 * ((g >> 3) & 1) + 256 * u);
+      }
+    }
   };
 
   // Fragment read: lane's row `r` of a 128-byte-row tile, chunks quarter and
@@ -257,13 +270,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   // Pipeline: step g computes from stage g % STAGES while the copies of the
   // next STAGES - 1 steps are in flight. Copies are issued unconditionally
   // (steps past the end re-copy the last step into a stage that is never
-  // read again), so every step has the same constant wait: step g + 1 must
-  // have landed, the STAGES - 2 later ones may not.
-  // (a wave's own copies: the scale-copying waves issue one more per step)
+  // read again, and its scales unchanged), so the wait after a step is
+  // constant but for the scale copies: step g + 1 must have landed, the
+  // STAGES - 2 later ones (with 8-group scale copies when their group is a
+  // multiple of 8) may not.
   constexpr int kInFlight = (STAGES - 2) * KC::kTileLoadsPerWave;
-  constexpr int kInFlightScales = (STAGES - 2) * (KC::kTileLoadsPerWave + 1);
-  auto wait_step = [&]() {
-    if (copies_scales) wait_vm_barrier<kInFlightScales>();
+  constexpr int kInFlightScales = kInFlight + (STAGES - 2) * S_CHUNKS;
+  auto wait_step = [&](bool scales_in_flight) {
+    if (STAGES > 2 && scales_in_flight) wait_vm_barrier<kInFlightScales>();
     else wait_vm_barrier<kInFlight>();
   };
   using S0 = std::integral_constant<int, 0>;
@@ -271,17 +285,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   using S2 = std::integral_constant<int, 2>;
   issue(0, S0{});
   if constexpr (STAGES == 3) issue(groups > 1 ? 1 : 0, S1{});
-  wait_step();
+  wait_step(false);
 
   auto step = [&](int64_t g, auto st) {
     constexpr int cur = decltype(st)::value;
     constexpr int nxt = (cur + STAGES - 1) % STAGES;  // stage of step g + STAGES - 1
-    const int64_t gn = g + STAGES - 1;
-    issue(gn < groups ? gn : groups - 1, std::integral_constant<int, nxt>{});
+    const int64_t gn = g + STAGES - 1 < groups ? g + STAGES - 1 : groups - 1;
+    issue(gn, std::integral_constant<int, nxt>{});
 
     const unsigned char* la = stage_base(st);
     const unsigned char* lw = la + BM * 128;
-    const float* ls = reinterpret_cast<const float*>(la + (BM + BN) * 128);
+    const float* ls = lds_scales + BM * 8 * ((g >> 3) & 1) + (g & 7);
     const float sw = sw_src[g];
 
     v8i wf[I];
@@ -293,7 +307,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
     v4f p_prev[I];
     float sc_prev = 0.f;
     v8i af = frag(la, TM * wave_m + lrow);
-    float sc = ls[TM * wave_m + lrow] * sw;
+    float sc = ls[8 * (TM * wave_m + lrow)] * sw;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       v8i af_next = af;
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
       if (j + 1 < J) {
         const int tr = TM * wave_m + 16 * (j + 1) + lrow;
         af_next = frag(la, tr);
-        sc_next = ls[tr] * sw;
+        sc_next = ls[8 * tr] * sw;
       }
       // MFMA (i, j), then the scale FMAs of (i, j - 1), whose MFMA was issued
       // I MFMAs earlier: at most I + 1 fresh results are live.
@@ -341,7 +355,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
 
     // Step g + 1's copies must have landed, and every wave must be done
     // reading this stage before the next step's copies overwrite it.
-    wait_step();
+    wait_step((gn & 7) == 0);
   };
 
   for (int64_t g = 0; g < groups; g += STAGES) {
