@@ -231,14 +231,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
     else return lds2;
   };
 
-  auto issue = [&](int64_t g, auto st) {
+  // The copies of group g into stage st: this wave's 8-row chunks c = 0 ..
+  // A_CHUNKS - 1 of the token tile, then A_CHUNKS .. CHUNKS - 1 of the
+  // weight tile; every 8 groups also the scales.
+  constexpr int CHUNKS = A_CHUNKS + W_CHUNKS;
+  constexpr bool kSpread = I * J >= 8;
+  auto issue_chunk = [&](int64_t g, auto st, int c) {
     unsigned char* base = stage_base(st);
-    const void* ag = uniform(a_base + g * kGroup);
-    const void* wg = uniform(w_base + g * kGroup);
-#pragma unroll
-    for (int q = 0; q < A_CHUNKS; ++q) dma16(ag, a_off[q], base + 1024 * (wave + WAVES * q));
-#pragma unroll
-    for (int q = 0; q < W_CHUNKS; ++q) dma16(wg, w_off[q], base + BM * 128 + 1024 * (wave + WAVES * q));
+    if (c < A_CHUNKS)
+      dma16(uniform(a_base + g * kGroup), a_off[c], base + 1024 * (wave + WAVES * c));
+    else
+      dma16(uniform(w_base + g * kGroup), w_off[c - A_CHUNKS], base + BM * 128 + 1024 * (wave + WAVES * (c - A_CHUNKS)));
+  };
+  auto issue_scales = [&](int64_t g) {
     if ((g & 7) == 0) {  // the scales of groups g .. g + 7
       const int64_t col = g_lo + g + (lane & 7) < gstride ? g_lo + g + (lane & 7) : gstride - 1;
 #pragma unroll
@@ -250,6 +255,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
              reinterpret_cast<unsigned char*>(lds_scales) + 4 * BM * 8 * ((g >> 3) & 1) + 256 * u);
       }
     }
+  };
+  auto issue = [&](int64_t g, auto st) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) issue_chunk(g, st, c);
+    issue_scales(g);
   };
 
   // Fragment read: lane's row `r` of a 128-byte-row tile, chunks quarter and
@@ -290,8 +300,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
   auto step = [&](int64_t g, auto st) {
     constexpr int cur = decltype(st)::value;
     constexpr int nxt = (cur + STAGES - 1) % STAGES;  // stage of step g + STAGES - 1
+    using SN = std::integral_constant<int, nxt>;
     const int64_t gn = g + STAGES - 1 < groups ? g + STAGES - 1 : groups - 1;
-    issue(gn, std::integral_constant<int, nxt>{});
+    // The tile chunks now where a wave's step is short (4 MFMAs: 64 x 64
+    // tiles), else spread over sub-tile 0's MFMAs, and the scales: a burst of
+    // copies at the step's start holds up the MFMAs (M = 512..1024 on the
+    // logged shapes: 128 x 128 and 128 x 256 tiles 6-10% faster; 64 x 64
+    // tiles 9-11% slower spread).
+    if constexpr (!kSpread) {
+#pragma unroll
+      for (int c = 0; c < CHUNKS; ++c) issue_chunk(gn, SN{}, c);
+    }
+    issue_scales(gn);
 
     const unsigned char* la = stage_base(st);
     const unsigned char* lw = la + BM * 128;
@@ -323,6 +343,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
 #pragma unroll
       for (int i = 0; i < I; ++i) {
         p_cur[i] = mfma_16x16x128_e4m3(wf[i], af);
+        if (kSpread && j == 0) {
+#pragma unroll
+          for (int c = i * CHUNKS / I; c < (i + 1) * CHUNKS / I; ++c) issue_chunk(gn, SN{}, c);
+        }
         if (j > 0) {
           acc[i][j - 1][0] = fmaf(sc_prev, p_prev[i][0], acc[i][j - 1][0]);
           acc[i][j - 1][1] = fmaf(sc_prev, p_prev[i][1], acc[i][j - 1][1]);
