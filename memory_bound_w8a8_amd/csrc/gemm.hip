@@ -334,7 +334,7 @@ constexpr TileShape kTileShapes[] = {
     {128, 128, 1, 85, 85, "gemm_tiled_kernel BM=128 BN=128 4 waves 3 stages"},
     {128, 256, 1, 115, 115, "gemm_tiled_kernel BM=128 BN=256 8 waves 3 stages"},
     {192, 256, 1, 150, 150, "gemm_tiled2_kernel BM=192 BN=256 8 waves 2 stages", true, 126},
-    {256, 256, 1, 190, 190, "gemm_tiled2_kernel BM=256 BN=256 8 waves 2 stages", true, 160},
+    {256, 256, 1, 178, 178, "gemm_tiled2_kernel BM=256 BN=256 8 waves 2 stages", true, 140},
     {64, 128, 2, 60, 100, "gemm_tiled_kernel BM=64 BN=128 4 waves 3 stages"},
     {128, 64, 2, 60, 100, "gemm_tiled_kernel BM=128 BN=64 4 waves 3 stages"},
     {64, 64, 3, 52, 90, "gemm_tiled_kernel BM=64 BN=64 4 waves 3 stages"},

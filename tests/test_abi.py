@@ -361,7 +361,7 @@ def test_measurement_kernel_argument_errors(fp8bq):
 
 def test_tile_shape_rule_takes_the_measured_choices(fp8bq):
     """The tiled kernel's shape rule (least grid rounds x measured step
-    cost) on the 25 points where the shapes were timed side by side (each
+    cost) on points where the shapes were timed side by side (each
     expectation is the shape that measured fastest there), then its
     tie-break and its range."""
     L = fp8bq.lib()
@@ -372,6 +372,10 @@ def test_tile_shape_rule_takes_the_measured_choices(fp8bq):
     assert shape(4096, 7168, 5120) == "tiled 256x256"
     assert shape(1024, 8192, 5120) == "tiled 128x256"
     assert shape(1024, 17408, 5120) == "tiled 192x256"
+    assert shape(3072, 17408, 5120) == "tiled 256x256"  # 274 us against 301 for 192 x 256
+    assert shape(4096, 17408, 5120) == "tiled 256x256"  # 355 against 376
+    assert shape(2048, 17408, 5120) == "tiled 192x256"  # 180 against 195
+    assert shape(2560, 5120, 8704) == "tiled 256x256"
     for m in (65, 96, 128):
         assert shape(m, 17408, 5120) == "tiled 128x128", m  # 136 tiles; smaller ones overflow a round
         for n, k in ((5120, 3072), (5120, 8704), (7168, 5120), (8192, 5120)):
