@@ -57,9 +57,11 @@ template <int MT, int AF, int TILES, int GMAX, int TOK = 16>
 hipError_t rows_instance(const GemmArgs& a, int64_t rows_per_wg) {
   // chunks of weight loads kept in flight per wave (fewer where the held
   // activation of a 32-token tile, or the bf16 activation awaiting
-  // quantisation, already takes most registers)
+  // quantisation, already takes most registers; and at 8..9 groups per wave
+  // with the activation codes held for every group: on (5120, 8704) at
+  // M = 1..8, 2 in flight measured 2-4% faster than 6, 1, 3 or 4)
   constexpr int PD = AF == kActBf16 ? (GMAX >= 8 ? 2 : (GMAX >= 7 ? 4 : 6))
-                                    : (MT == 16 ? 6 : 4);
+                                    : (MT == 16 ? (AF == kActCodes && GMAX >= 8 ? 2 : 6) : 4);
   const unsigned grid = static_cast<unsigned>((a.n + rows_per_wg - 1) / rows_per_wg);
   hipLaunchKernelGGL((gemm_rows_kernel<MT, kRowsWaves, GMAX, TILES, PD, AF, TOK>), dim3(grid), dim3(64 * kRowsWaves),
                      0, a.stream, static_cast<int>(a.m), a.n, a.k, rows_per_wg,
