@@ -9,13 +9,14 @@
 // Tiling. A workgroup of WM x WN waves computes a BM x BN tile of C (tokens x
 // weight rows); each wave owns a (BM / WM) x (BN / WN) sub-tile held in fp32
 // registers. K is walked one 128-wide scale group per step:
-//   1. the step's A slice (BM x 128 codes), W slice (BN x 128 codes) and the
-//      BM activation scales are copied global -> LDS with direct-to-LDS loads
-//      (no registers), STAGES deep: steps g + 1 .. g + STAGES - 1 are in
-//      flight while step g computes (three stages where they fit in the
-//      160 KB of LDS, two for the 192- and 256-token tiles). The scales of
-//      one group are a strided gather (one line per token), so only BM / 64
-//      waves copy them;
+//   1. the step's A slice (BM x 128 codes) and W slice (BN x 128 codes) are
+//      copied global -> LDS with direct-to-LDS loads (no registers), STAGES
+//      deep: steps g + 1 .. g + STAGES - 1 are in flight while step g
+//      computes (three stages where they fit in the 160 KB of LDS, two for
+//      the 192- and 256-token tiles); the copies go out spread over a
+//      sub-tile's MFMAs rather than in one burst. The BM activation scales
+//      come 8 groups at a time (a BM x 8 block every 8 steps, 8 rows per
+//      copy instruction) into a two-buffer array of their own;
 //   2. each wave reads its W fragments once per step and streams its token
 //      fragments; one 16x16x128 FP8 MFMA per 16 x 16 sub-tile gives the
 //      group's exact products into a fresh accumulator (weight rows first
