@@ -192,6 +192,29 @@ def test_tile_shapes_whole_output_and_bitwise(m, n, k):
         assert torch.equal(c.view(torch.int16), outs[0].view(torch.int16)), f"tile path {path}"
 
 
+# The tiled kernels copy the activation scales 8 groups at a time into a
+# two-buffer array: K/128 = 13 and 17 groups end on a partly filled block of
+# 8 (columns past the last group clamped), 17 also reuses the first buffer.
+# Whole output against the oracle for the 8-wave tiles on their unclamped
+# path (M >= BM, N a multiple of 256, the last token tile shifted back) and
+# clamped path (N = 520), bitwise equal to 128 x 128 and 64 x 64 tiles.
+@pytest.mark.parametrize("k", [13 * 128, 17 * 128])
+@pytest.mark.parametrize("n", [512, 520])
+def test_tiled_scale_blocks_partial_last(n, k):
+    m = 300
+    a_q, a_s, w_q, w_s = _problem(m, n, k)
+    ref = gemm_ref(a_q, a_s, w_q, w_s)
+    args = [to_gpu(a_q), to_gpu(a_s), to_gpu(w_q), to_gpu(w_s)]
+    outs = {}
+    for path in (fp8bq.PATH_TILED_256x256, fp8bq.PATH_TILED_192x256, fp8bq.PATH_TILED_128x128,
+                 fp8bq.PATH_TILED_64x64):
+        outs[path] = fp8bq.gemm_forced(path, *args)
+    torch.cuda.synchronize()
+    for path, c in outs.items():
+        assert_gemm_close(bf16_to_f64(c), ref, what=f"tile path {path} N={n} K={k}")
+        assert torch.equal(c.view(torch.int16), outs[fp8bq.PATH_TILED_128x128].view(torch.int16)), f"tile path {path}"
+
+
 # Grids of the 8-wave tiles with a last round of at most 128 tiles run that
 # round as column halves (a second launch of BM x BN/2 workgroups): whole
 # output against the oracle and bitwise equal to 128 x 128 tiles, for the
