@@ -456,7 +456,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(int64_t m_rows
 //    after the barrier a wave issues the next step's copies and fragment
 //    reads, then those MFMAs (operands already in registers), which cover
 //    the latency of the new reads; each weight fragment is refilled right
-//    after the MFMA that last uses it.
+//    after the MFMA that last uses it. Where no row is clamped, half of
+//    step g + 2's copies go out there and the other half with step g + 1's
+//    first sub-tile (the clamped instance has no registers left for the
+//    second set of lane offsets and issues them all after the barrier).
 //  - The two waves that share a SIMD would otherwise take the matrix core in
 //    age order (a per-wave timestamp trace showed the older wave finishing
 //    its K step about 1,000 cycles before the younger one, which then ran
@@ -582,6 +585,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
   // A_CHUNKS - 1 of the token tile, then A_CHUNKS .. CHUNKS - 1 of the
   // weight tile, and (waves 0 .. BM / 64 - 1) the token scales.
   constexpr int CHUNKS = A_CHUNKS + W_CHUNKS;
+  constexpr bool kSplitCopies = !CLAMP;
+  constexpr int HALF = kSplitCopies ? CHUNKS / 2 : CHUNKS;  // chunks issued with the deferred sub-tile
   auto issue_chunk = [&](int64_t g, auto st, int c) {
     unsigned char* base = stage_base(st);
     if (c < A_CHUNKS) {
@@ -682,42 +687,57 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled2_kernel(int64_t m_row
   auto step = [&](int64_t g, auto st) {
     constexpr int cur = decltype(st)::value;
     using SN = std::integral_constant<int, cur ^ 1>;
+    // Unclamped, the second half of step g + 1's copies (into the other
+    // stage) go out with sub-tile 0 (the first went out with step g - 1's
+    // deferred sub-tile; the prologue copied group 1 whole); clamped, its
+    // per-copy lane offsets leave no registers for that and all go out with
+    // the deferred sub-tile.
+    const bool second_half = kSplitCopies && g >= 1 && g + 1 < groups;
 #pragma unroll
     for (int j = 0; j < J - 1; ++j) {
       const v8i af_n = a_frag(st, j + 1);
       const float sa_n = a_scale(g, j + 1);
       set_prio(3 - (3 * (j + 1)) / (J - 1));
-      mfma_row((j + J - 1) % J, sa * sw, nothing);
-      af = af_n;
-      sa = sa_n;
-    }
-    if (g + 1 < groups) {
-      if (((g + 1) & 63) == 0) sw_lanes = sw_chunk(g + 1);
-      const float sw_n = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw_lanes),
-                                                                             static_cast<int>((g + 1) & 63)));
-      // every LDS read of this stage has completed and step g + 1's tiles
-      // have landed (own copies: vmcnt; everyone's: the barrier)
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      set_prio(3);
-      // step g + 2's copies, spread over the deferred sub-tile's MFMAs
-      // (issued at once after the barrier, every wave's burst of copies
-      // held up its MFMAs: 3.5% more cycles per K step)
-      const int64_t g2 = g + 2 < groups ? g + 2 : groups - 1;
-      if (g + 2 < groups && (g2 & 7) == 0) issue_scales(g2);
-      const v8i af_n = a_frag(SN{}, 0);
-      const float sa_n = a_scale(g + 1, 0);
-      mfma_row(J - 2, sa * sw, [&](int i) {
-        wf[i] = w_frag(SN{}, i);
+      mfma_row((j + J - 1) % J, sa * sw, [&](int i) {
+        if (j == 0 && second_half) {
 #pragma unroll
-        for (int c = i * CHUNKS / I; c < (i + 1) * CHUNKS / I; ++c) issue_chunk(g2, st, c);
+          for (int c = HALF + i * (CHUNKS - HALF) / I; c < HALF + (i + 1) * (CHUNKS - HALF) / I; ++c)
+            issue_chunk(g + 1, SN{}, c);
+        }
       });
       af = af_n;
       sa = sa_n;
-      sw = sw_n;
-    } else {
-      mfma_row(J - 2, sa * sw, nothing);
     }
+    // The same code at every step, the last included (its fragment reads
+    // after the barrier fetch a stage that holds nothing of use, and are
+    // not used): with a separate branch for the last step the compiler
+    // renamed the running sums across the two paths and moved them back,
+    // about 30 register moves per step.
+    const bool more = g + 1 < groups;
+    if (more && ((g + 1) & 63) == 0) sw_lanes = sw_chunk(g + 1);
+    const float sw_n = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw_lanes),
+                                                                           static_cast<int>((g + 1) & 63)));
+    // every LDS read of this stage has completed and step g + 1's tiles
+    // have landed (own copies: vmcnt; everyone's: the barrier)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    set_prio(3);
+    // step g + 2's copies, spread over the deferred sub-tile's MFMAs
+    // (issued at once after the barrier, every wave's burst of copies
+    // held up its MFMAs: 3.5% more cycles per K step); past the last group
+    // a copy of it into the stage just consumed, never read
+    const int64_t g2 = g + 2 < groups ? g + 2 : groups - 1;
+    if (g + 2 < groups && (g2 & 7) == 0) issue_scales(g2);
+    const v8i af_n = a_frag(SN{}, 0);
+    const float sa_n = a_scale(g + 1, 0);
+    mfma_row(J - 2, sa * sw, [&](int i) {
+      wf[i] = w_frag(SN{}, i);
+#pragma unroll
+      for (int c = i * HALF / I; c < (i + 1) * HALF / I; ++c) issue_chunk(g2, st, c);
+    });
+    af = af_n;
+    sa = sa_n;
+    sw = sw_n;
   };
 
   for (int64_t g = 0; g < groups; g += 2) {
