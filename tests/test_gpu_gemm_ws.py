@@ -151,3 +151,24 @@ def test_default_plan_full_size_sampled(m, n, k, weights_on_gpu):
     got = bf16_to_f64(c[rows][:, torch.from_numpy(col_global).to(c.device)]).ravel()
     assert_gemm_close(got, ref, what=f"M={m} N={n} K={k} (split plan, workspace "
                                      f"{fp8bq.gemm_workspace_bytes(m, n, k)} B)")
+
+
+# The workspace's contents are arbitrary on entry: a workspace full of 0xff
+# bytes (NaN partial tiles) gives the same bits as a zeroed one, twice in a
+# row, with partial token and weight tiles, so no element of the workspace
+# is read before this call wrote it.
+@pytest.mark.parametrize("path, split", [(fp8bq.PATH_TILED_128x256, 3), (fp8bq.PATH_TILED_64x64, 5)])
+def test_forced_split_any_workspace_contents(path, split):
+    m, n, k = 65, 1000, 1280
+    a_q, a_s, w_q, w_s = _problem(m, n, k)
+    args = [to_gpu(x) for x in (a_q, a_s, w_q, w_s)]
+    need = split * m * n * 4
+    zeroed = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    dirty = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    c0 = fp8bq.gemm_ws_forced(path, split, *args, workspace=zeroed)
+    c1 = fp8bq.gemm_ws_forced(path, split, *args, workspace=dirty)
+    c2 = fp8bq.gemm_ws_forced(path, split, *args, workspace=dirty)
+    torch.cuda.synchronize()
+    assert torch.equal(c0.view(torch.int16), c1.view(torch.int16))
+    assert torch.equal(c0.view(torch.int16), c2.view(torch.int16))
+    assert_gemm_close(bf16_to_f64(c0), gemm_ref(a_q, a_s, w_q, w_s), what=f"path {path} split {split}")
